@@ -1,0 +1,155 @@
+/*
+ * libmuseattn -- one attention step of gated grouped-query attention over a
+ * paged FP8 E4M3 KV cache, for AMD Instinct MI355X (gfx950).
+ *
+ * The operation is the one defined on the task page "Gated attention decode
+ * (muse_attention_decode)", section "What to compute": for every request b
+ * and block token j (position p = positions[b*L + j]) of one decode step
+ * (L = 1) or one causal verify block (L <= 8):
+ *
+ *   q, k, v, gate = split(qkv row)              (section "What to compute")
+ *   q = rmsnorm(q) * w_q * q_scale ; k = rmsnorm(k) * w_k
+ *   q, k = rope(q, p), rope(k, p)               sliding-window layers only
+ *   cache row(b, p) <- fp8(k / kv_scale), fp8(v / kv_scale)
+ *   a = softmax(q . K^T / 8) . V                keys 0..p (full layer) or
+ *                                               p-2047..p (sliding layer,
+ *                                               section "Shapes")
+ *   out = rmsnorm(a) * w_o * sigmoid(gate)      per head, bf16
+ *
+ * Shapes per GPU shard (section "Shapes"): 16 query heads, 2 KV heads, head
+ * dim 64; query head h reads KV head h / 8.  The fused row is bf16
+ * [q 16x64 | k 2x64 | v 2x64 | gate 16x64] = 2304 values.
+ *
+ * Paged cache (section "Shapes": E4M3 bytes, page size 1 or 64, a scale of
+ * 1 or 1/64): k_cache and v_cache are separate byte arrays of num_rows rows;
+ * a row holds one token's two KV heads, [2][64] E4M3FN bytes = 128 B.  With
+ * page size ps, row(b, u) = table[b*table_stride + u/ps]*ps + u%ps: at ps = 1
+ * the table holds one cache row per position ("cache_loc"); at ps = 64 it
+ * holds page ids and a page is 64 consecutive rows.  The new tokens' rows are
+ * found through the same table, so the caller allocates them (as a serving
+ * engine does) before the call.
+ *
+ * Call contract (section "Rules": CUDA graphs, fresh inputs):
+ *  - every pointer argument except `params` and `stream` is DEVICE memory
+ *    owned by the caller; `params` is a host struct read during the call.
+ *  - the library never allocates, frees, synchronises or reads device values
+ *    on the host; all work is enqueued on `stream`, so a call can be captured
+ *    into a HIP graph.  Nothing is cached between calls.
+ *  - k_cache / v_cache are written only at the B*L new rows; `out` must not
+ *    overlap `qkv`; `workspace` holds scratch data of one call (it must not be
+ *    shared by calls that may run concurrently).
+ *  - device-side indices are clamped into the extents the host validated
+ *    (rows into [0, num_rows), positions into [0, max_seq_len)), so
+ *    inconsistent device data gives wrong numbers, never an out-of-bounds
+ *    access.  seq_lens[b] must not exceed max_seq_len; keys beyond it are not
+ *    attended.
+ *
+ * Errors: 0 on success; a negative museattn_status if host-side validation
+ * fails, in which case nothing was enqueued; MUSEATTN_ERR_LAUNCH if a kernel
+ * launch reported an error (hipGetLastError).
+ */
+#ifndef MUSEATTN_H
+#define MUSEATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MUSEATTN_ABI_VERSION 1
+
+/* Layer kinds (task page, section "Shapes"): a full-attention layer sees the
+ * whole context and uses no RoPE; a sliding-window layer sees the last 2048
+ * positions (the query's own included) and rotates q and k. */
+enum museattn_layer_kind { MUSEATTN_FULL = 0, MUSEATTN_SLIDING = 1 };
+
+#define MUSEATTN_WINDOW 2048
+#define MUSEATTN_QKV_WIDTH 2304
+#define MUSEATTN_OUT_WIDTH 1024
+#define MUSEATTN_ROW_BYTES 128
+
+enum museattn_status {
+  MUSEATTN_OK = 0,
+  MUSEATTN_ERR_NULL = -1,         /* a required pointer is null */
+  MUSEATTN_ERR_PAGE_SIZE = -2,    /* page_size is not 1 or 64 */
+  MUSEATTN_ERR_LAYER_KIND = -3,   /* layer_kind is not FULL or SLIDING */
+  MUSEATTN_ERR_SHAPE = -4,        /* B, L, max_seq_len or num_rows out of range */
+  MUSEATTN_ERR_TABLE = -5,        /* table_stride < ceil(max_seq_len / page_size) */
+  MUSEATTN_ERR_ALIGN = -6,        /* k_cache/v_cache not 16-byte aligned, or
+                                     qkv/out/weights not naturally aligned */
+  MUSEATTN_ERR_WORKSPACE = -7,    /* workspace smaller than museattn_workspace_bytes()
+                                     or not 256-byte aligned */
+  MUSEATTN_ERR_PARAM = -8,        /* kv_scale, eps, q_scale, rope_base or
+                                     split_keys out of range */
+  MUSEATTN_ERR_ALIAS = -9,        /* out overlaps qkv */
+  MUSEATTN_ERR_LAUNCH = -10       /* a kernel launch failed */
+};
+
+/* Constants of the step that the page fixes or that the computation needs
+ * but the page's input list leaves implicit (all read on the host). */
+typedef struct museattn_params {
+  const float *q_norm_w;   /* device float32 [64]: per-dim weight of q's rmsnorm */
+  const float *k_norm_w;   /* device float32 [64]: per-dim weight of k's rmsnorm */
+  const float *o_norm_w;   /* device float32 [64]: per-dim weight of the output rmsnorm */
+  float eps;               /* rmsnorm epsilon, >= 0 (1e-6) */
+  float q_scale;           /* multiplier of the normed q (5.473) */
+  float rope_base;         /* RoPE base, > 0 (10000) */
+  int split_keys;          /* keys per work-group along the key axis; 0 = chosen
+                              from the shapes, else a multiple of 32 in
+                              [32, 4096]. */
+} museattn_params;
+
+/* Bytes of device workspace museattn_attn_step needs for these shapes (a
+ * function of its arguments only).  Returns 0 if the arguments are invalid. */
+size_t museattn_workspace_bytes(int B, int L, int max_seq_len, int page_size, int layer_kind,
+                                const museattn_params *params);
+
+/* Host-side validation of museattn_attn_step's arguments, without touching
+ * the device (pointers are checked for null, alignment and overlap only).
+ * Returns MUSEATTN_OK or the status museattn_attn_step would return. */
+int museattn_check_args(const void *qkv, const int32_t *positions, const int32_t *table,
+                        const int32_t *seq_lens, const void *k_cache, const void *v_cache,
+                        float kv_scale, int page_size, int layer_kind, const void *out,
+                        int B, int L, int table_stride, int max_seq_len, int64_t num_rows,
+                        const museattn_params *params, const void *workspace,
+                        size_t workspace_bytes);
+
+/* One attention step (the operation described at the top of this file).
+ *   qkv        bf16 [B*L][2304], row t = b*L + j
+ *   positions  int32 [B*L], p of token t (normally seq_lens[b] - L + j)
+ *   table      int32 [B][table_stride]: rows (page_size 1) or page ids (64)
+ *   seq_lens   int32 [B]: cached tokens + L ("FA3 lengths"), <= max_seq_len
+ *   k_cache,
+ *   v_cache    E4M3FN bytes [num_rows][2][64], 16-byte aligned; the B*L
+ *              rows row(b, positions[t]) are written, all other rows read-only
+ *   kv_scale   > 0: stored byte = fp8(x / kv_scale); read value = byte * kv_scale
+ *   page_size  1 or 64
+ *   layer_kind MUSEATTN_FULL or MUSEATTN_SLIDING
+ *   out        bf16 [B][L][1024]
+ *   stream     hipStream_t the work is enqueued on (NULL = default stream)
+ *   B >= 1, 1 <= L <= 8, table_stride >= ceil(max_seq_len / page_size),
+ *   L <= max_seq_len <= 2^30, num_rows a multiple of page_size,
+ *   workspace  device scratch of >= museattn_workspace_bytes(...) bytes,
+ *              256-byte aligned. */
+int museattn_attn_step(const void *qkv, const int32_t *positions, const int32_t *table,
+                       const int32_t *seq_lens, void *k_cache, void *v_cache, float kv_scale,
+                       int page_size, int layer_kind, void *out, void *stream, int B, int L,
+                       int table_stride, int max_seq_len, int64_t num_rows,
+                       const museattn_params *params, void *workspace, size_t workspace_bytes);
+
+/* Keys per split the library uses for these shapes (split_keys = 0 chooses). */
+int museattn_split_keys(int B, int L, int max_seq_len, int layer_kind, const museattn_params *params);
+
+/* Static description of a status code. */
+const char *museattn_strerror(int status);
+
+/* MUSEATTN_ABI_VERSION of the built library. */
+int museattn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MUSEATTN_H */

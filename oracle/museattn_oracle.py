@@ -95,6 +95,10 @@ def e4m3_encode(x) -> np.ndarray:
     return (code | sign).astype(np.uint8)
 
 
+# value of every byte, for table-lookup dequantisation of long key ranges
+_DECODE_TABLE = e4m3_decode(np.arange(256))
+
+
 def e4m3_ordinal(codes) -> np.ndarray:
     """Signed position of a code on the E4M3 number line (+0 and -0 both 0).
 
@@ -203,19 +207,23 @@ def attend(q, k_pool, v_pool, table, positions, B, L, page_size, kv_scale, windo
     ks = float(kv_scale)
     a = np.zeros((B * L, HQ, D))
     for b in range(B):
+        # the union of the block tokens' key ranges, read and dequantised once
+        spans = [visible_keys(int(positions[b * L + j]), window) for j in range(L)]
+        ulo = min(lo for lo, _ in spans)
+        uhi = max(hi for _, hi in spans)
+        rows = cache_row(table, b, np.arange(ulo, uhi + 1), page_size)
+        kd = _DECODE_TABLE[k_pool[rows]] * ks          # [n, 2, 64]
+        vd = _DECODE_TABLE[v_pool[rows]] * ks
         for j in range(L):
             t = b * L + j
-            p = int(positions[t])
-            lo, hi = visible_keys(p, window)
-            rows = cache_row(table, b, np.arange(lo, hi + 1), page_size)
-            kd = e4m3_decode(k_pool[rows]) * ks          # [n, 2, 64]
-            vd = e4m3_decode(v_pool[rows]) * ks
+            lo, hi = spans[j]
+            kj, vj = kd[lo - ulo:hi - ulo + 1], vd[lo - ulo:hi - ulo + 1]
             for h in range(HQ):
                 g = h // GROUP
-                s = kd[:, g, :] @ q[t, h] / SOFTMAX_DIV
+                s = kj[:, g, :] @ q[t, h] / SOFTMAX_DIV
                 m = np.max(s)
                 e = np.exp(s - m)
-                a[t, h] = (e @ vd[:, g, :]) / np.sum(e)
+                a[t, h] = (e @ vj[:, g, :]) / np.sum(e)
     return a
 
 

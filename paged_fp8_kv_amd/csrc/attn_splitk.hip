@@ -1,0 +1,353 @@
+// Split-K attention over the paged FP8 cache: softmax(q . K^T / 8) . V for
+// every block token and query head (task page "Gated attention decode",
+// section "What to compute", line a = softmax(...); window and causal rules
+// from section "Shapes").  Each work-group owns one split of one request's
+// key axis and writes one partial (running max, sum, unnormalised output) per
+// (token, head); the combine kernel merges the splits.
+//
+// Data path per 32-key chunk (one wave):
+//  * cache rows come from an LDS copy of the split's table entries, so the
+//    dependent index load never stalls the row loads;
+//  * K rows: lane (n = lane%16, j = lane/16) loads 16 B of key n's row at
+//    byte 16j (KV head 0) and 64+16j (KV head 1) -- the A operand of
+//    S^T = K . Q^T on v_mfma_f32_16x16x32_bf16 (fp8 -> bf16 is exact);
+//  * Q^T is block-diagonal: head n's column is zero on the other KV head's
+//    dims, and q is carried as bf16 hi + lo (two MFMAs) so the product keeps
+//    ~16 significant bits of q;
+//  * the S^T tile leaves head n's scores for keys 4j..4j+3 (and 16+4j..) in
+//    lane (n, j): exactly the B operand layout of O^T = V^T . P^T, so P needs
+//    no data movement (P is carried as bf16 hi + lo as well);
+//  * V^T is the A operand of that product: lane (n, j) loads 8 B (dims
+//    8n..8n+7 of both KV heads) of the 8 keys it holds P for, and an 8x8 byte
+//    transpose in registers turns them into 8 M-tiles (row n of M-tile mt =
+//    byte 8n+mt of the V row);
+//  * online softmax in base 2 (log2(e)/8 and kv_scale are folded into q).
+//
+// Decode (L = 1): the 4 waves take interleaved chunks of the split and merge
+// their states in LDS.  Verify (L > 1): wave w owns tokens w and w+4 and
+// walks every chunk of the split (the re-reads of a row by the 4 waves hit
+// the cache).
+#include "device_common.h"
+#include "launch.h"
+
+namespace museattn {
+
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr int MAX_SPLIT_LDS = 4096;   // table entries cached per work-group
+
+struct RowBuf {
+  uint4 k[4];   // [tile*2 + kv head] 16 B of K row
+  uint2 v[8];   // 8 B of V rows of the 8 keys this lane holds P for
+};
+
+struct TokState {
+  f32x4 o[8];   // O^T accumulators, M-tile mt = bytes 8*row + mt of the V row
+  float m;      // running max (log2 units), same in the 4 lanes of a head
+  float l;      // this lane's share of the running sum
+  int lo, hi;   // visible key positions of the token, inclusive
+  bool live;
+};
+
+struct QOps {
+  bf16x8 hi[4], lo[4];   // B operand of S^T per K-step
+};
+
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t x, uint32_t y) {
+  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, false);
+  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, true);
+  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(y, 1.0f, false);
+  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(y, 1.0f, true);
+  bf16x8 r;
+  r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
+  r[4] = c[0]; r[5] = c[1]; r[6] = d[0]; r[7] = d[1];
+  return r;
+}
+
+// 4x4 byte transpose: y_k byte i = x_i byte k.
+__device__ __forceinline__ void transpose4x4(uint32_t x0, uint32_t x1, uint32_t x2, uint32_t x3,
+                                             uint32_t &y0, uint32_t &y1, uint32_t &y2,
+                                             uint32_t &y3) {
+  const uint32_t t0 = __builtin_amdgcn_perm(x1, x0, 0x05010400u);  // x0b0 x1b0 x0b1 x1b1
+  const uint32_t t1 = __builtin_amdgcn_perm(x1, x0, 0x07030602u);  // x0b2 x1b2 x0b3 x1b3
+  const uint32_t t2 = __builtin_amdgcn_perm(x3, x2, 0x05010400u);
+  const uint32_t t3 = __builtin_amdgcn_perm(x3, x2, 0x07030602u);
+  y0 = __builtin_amdgcn_perm(t2, t0, 0x05040100u);
+  y1 = __builtin_amdgcn_perm(t2, t0, 0x07060302u);
+  y2 = __builtin_amdgcn_perm(t3, t1, 0x05040100u);
+  y3 = __builtin_amdgcn_perm(t3, t1, 0x07060302u);
+}
+
+// Max / sum over the 4 lanes n, n+16, n+32, n+48 (one head's lanes).
+__device__ __forceinline__ float head_max(float x) {
+  int xi = __float_as_int(x);
+  auto p = __builtin_amdgcn_permlane16_swap(xi, xi, false, false);
+  x = fmaxf(__int_as_float(p[0]), __int_as_float(p[1]));
+  xi = __float_as_int(x);
+  auto q = __builtin_amdgcn_permlane32_swap(xi, xi, false, false);
+  return fmaxf(__int_as_float(q[0]), __int_as_float(q[1]));
+}
+
+__device__ __forceinline__ float head_sum(float x) {
+  int xi = __float_as_int(x);
+  auto p = __builtin_amdgcn_permlane16_swap(xi, xi, false, false);
+  x = __int_as_float(p[0]) + __int_as_float(p[1]);
+  xi = __float_as_int(x);
+  auto q = __builtin_amdgcn_permlane32_swap(xi, xi, false, false);
+  return __int_as_float(q[0]) + __int_as_float(q[1]);
+}
+
+__device__ __forceinline__ void load_rows(RowBuf &rb, const uint8_t *__restrict__ kc,
+                                          const uint8_t *__restrict__ vc,
+                                          const uint32_t *lrows, int n, int j) {
+  const uint32_t k0 = lrows[n];
+  const uint32_t k1 = lrows[16 + n];
+  const uint4 va = *reinterpret_cast<const uint4 *>(lrows + 4 * j);
+  const uint4 vb = *reinterpret_cast<const uint4 *>(lrows + 16 + 4 * j);
+  const uint8_t *kp0 = kc + (uint64_t)k0 * ROW + 16 * j;
+  const uint8_t *kp1 = kc + (uint64_t)k1 * ROW + 16 * j;
+  rb.k[0] = *reinterpret_cast<const uint4 *>(kp0);
+  rb.k[1] = *reinterpret_cast<const uint4 *>(kp0 + 64);
+  rb.k[2] = *reinterpret_cast<const uint4 *>(kp1);
+  rb.k[3] = *reinterpret_cast<const uint4 *>(kp1 + 64);
+  const uint32_t vr[8] = {va.x, va.y, va.z, va.w, vb.x, vb.y, vb.z, vb.w};
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    rb.v[i] = *reinterpret_cast<const uint2 *>(vc + (uint64_t)vr[i] * ROW + 8 * n);
+}
+
+template <int NT>
+__device__ __forceinline__ void compute_chunk(const RowBuf &rb, int u0, int j,
+                                              TokState (&ts)[NT], const QOps (&q)[NT]) {
+  // K operands: tile t (keys 16t..16t+15), K-step kk = (KV head kk/2, 8-byte half kk%2)
+  bf16x8 ka[2][4];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    ka[t][0] = fp8x8_to_bf16(rb.k[2 * t].x, rb.k[2 * t].y);
+    ka[t][1] = fp8x8_to_bf16(rb.k[2 * t].z, rb.k[2 * t].w);
+    ka[t][2] = fp8x8_to_bf16(rb.k[2 * t + 1].x, rb.k[2 * t + 1].y);
+    ka[t][3] = fp8x8_to_bf16(rb.k[2 * t + 1].z, rb.k[2 * t + 1].w);
+  }
+  // V operands: 8x8 byte transpose (key slot i x dim-byte mt) then fp8 -> bf16
+  uint32_t tx[8], ty[8];
+  transpose4x4(rb.v[0].x, rb.v[1].x, rb.v[2].x, rb.v[3].x, tx[0], tx[1], tx[2], tx[3]);
+  transpose4x4(rb.v[0].y, rb.v[1].y, rb.v[2].y, rb.v[3].y, tx[4], tx[5], tx[6], tx[7]);
+  transpose4x4(rb.v[4].x, rb.v[5].x, rb.v[6].x, rb.v[7].x, ty[0], ty[1], ty[2], ty[3]);
+  transpose4x4(rb.v[4].y, rb.v[5].y, rb.v[6].y, rb.v[7].y, ty[4], ty[5], ty[6], ty[7]);
+  bf16x8 vb[8];
+#pragma unroll
+  for (int mt = 0; mt < 8; ++mt) vb[mt] = fp8x8_to_bf16(tx[mt], ty[mt]);
+
+#pragma unroll
+  for (int tk = 0; tk < NT; ++tk) {
+    TokState &st = ts[tk];
+    if (!st.live) continue;
+    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[0][kk], q[tk].hi[kk], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[1][kk], q[tk].hi[kk], s1, 0, 0, 0);
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[0][kk], q[tk].lo[kk], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[1][kk], q[tk].lo[kk], s1, 0, 0, 0);
+    }
+    float sc[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+    float cmax = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int u = u0 + (i >> 2) * 16 + 4 * j + (i & 3);
+      if (u < st.lo || u > st.hi) sc[i] = -INFINITY;
+      cmax = fmaxf(cmax, sc[i]);
+    }
+    cmax = head_max(cmax);
+    const float mnew = fmaxf(st.m, cmax);
+    const float muse = mnew == -INFINITY ? 0.0f : mnew;
+    const float alpha = __builtin_amdgcn_exp2f(st.m - muse);
+    if (__any(alpha != 1.0f)) {
+      st.l *= alpha;
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt) st.o[mt] *= alpha;
+    }
+    st.m = mnew;
+    bf16x8 ph, pl;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float pv = __builtin_amdgcn_exp2f(sc[i] - muse);
+      st.l += pv;
+      ph[i] = (__bf16)pv;
+      pl[i] = (__bf16)(pv - (float)ph[i]);
+    }
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) {
+      st.o[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vb[mt], ph, st.o[mt], 0, 0, 0);
+      st.o[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vb[mt], pl, st.o[mt], 0, 0, 0);
+    }
+  }
+}
+
+// B operand of S^T = K . Q^T for token t: lane (n, j), K-step kk holds
+// q[t][n][16j + 8(kk%2) + i] (i < 8) when head n belongs to KV head kk/2, else 0.
+__device__ __forceinline__ void load_q(const StepArgs &a, int t, int n, int j, float qmul,
+                                       QOps &qo) {
+  const float *qrow = a.qbuf + ((size_t)t * HQ + n) * D;
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    const bool mine = (n >> 3) == (kk >> 1);
+    const int d0 = 16 * j + 8 * (kk & 1);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float x = mine ? qrow[d0 + i] * qmul : 0.0f;
+      const __bf16 h = (__bf16)x;
+      qo.hi[kk][i] = h;
+      qo.lo[kk][i] = (__bf16)(x - (float)h);
+    }
+  }
+}
+
+template <int MODE, int NT, int NBUF>
+__global__ __launch_bounds__(256) void attn_splitk_kernel(StepArgs a) {
+  __shared__ __attribute__((aligned(16))) uint32_t lrows[MAX_SPLIT_LDS];
+  __shared__ float sm_m[WAVES][HQ];
+  __shared__ float sm_l[WAVES][HQ];
+  __shared__ __attribute__((aligned(16))) float sm_o[MODE == 0 ? WAVES : 1][HQ][D];
+
+  const int s = blockIdx.x, b = blockIdx.y;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int n = lane & 15, j = lane >> 4;
+
+  const KeyRange r = request_range(a, b);
+  if (s >= valid_splits(a, r)) return;   // uniform over the work-group
+  const int kstart = r.kbase + s * a.split_keys;
+  int kend = kstart + a.split_keys;
+  kend = kend < r.khi + 1 ? kend : r.khi + 1;
+  const int nchunks = (kend - kstart + CHUNK - 1) / CHUNK;
+
+  // cache rows of the split's keys (clamped into [klo, khi])
+  for (int i = tid; i < nchunks * CHUNK; i += 256) {
+    int u = kstart + i;
+    u = u < r.klo ? r.klo : (u > r.khi ? r.khi : u);
+    lrows[i] = cache_row(a, b, u);
+  }
+
+  const float qmul = a.kv_scale * (LOG2E / 8.0f);
+  TokState ts[NT];
+  QOps qo[NT];
+#pragma unroll
+  for (int tk = 0; tk < NT; ++tk) {
+    const int jt = MODE == 0 ? 0 : wave + WAVES * tk;
+    ts[tk].live = jt < a.L;
+    const int t = b * a.L + (ts[tk].live ? jt : 0);
+    const int p = a.positions[t];
+    ts[tk].hi = p < r.khi ? p : r.khi;
+    ts[tk].lo = a.sliding ? p - (WINDOW - 1) : 0;
+    ts[tk].m = -INFINITY;
+    ts[tk].l = 0.0f;
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) ts[tk].o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    load_q(a, t, n, j, qmul, qo[tk]);
+  }
+  __syncthreads();
+
+  const int c0 = MODE == 0 ? wave : 0;
+  const int cstep = MODE == 0 ? WAVES : 1;
+  bool any_live = false;
+#pragma unroll
+  for (int tk = 0; tk < NT; ++tk) any_live |= ts[tk].live;
+
+  if (any_live) {
+    RowBuf buf[NBUF];
+#pragma unroll
+    for (int k = 0; k < NBUF; ++k) {
+      const int c = c0 + k * cstep;
+      if (c < nchunks) load_rows(buf[k], a.k_cache, a.v_cache, lrows + c * CHUNK, n, j);
+    }
+    for (int c = c0; c < nchunks; c += NBUF * cstep) {
+#pragma unroll
+      for (int k = 0; k < NBUF; ++k) {
+        const int cc = c + k * cstep;
+        if (cc < nchunks) {
+          compute_chunk<NT>(buf[k], kstart + cc * CHUNK, j, ts, qo);
+          const int cn = cc + NBUF * cstep;
+          if (cn < nchunks) load_rows(buf[k], a.k_cache, a.v_cache, lrows + cn * CHUNK, n, j);
+        }
+      }
+    }
+  }
+
+  // Lane (n, j) holds O^T of head n at V-row bytes 8(4j + r) + mt, r < 4: KV head
+  // j/2, dims 32(j%2) + 8r + mt.  Only lanes whose KV head is head n's own hold
+  // meaningful values.
+  const bool own = (j >> 1) == (n >> 3);
+  const int dbase = 32 * (j & 1);
+  if (MODE == 0) {
+    const float lsum = head_sum(ts[0].l);
+    if (j == 0) {
+      sm_m[wave][n] = ts[0].m;
+      sm_l[wave][n] = lsum;
+    }
+    if (own) {
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        float *dst = &sm_o[wave][n][dbase + 8 * rr];
+        *reinterpret_cast<f32x4 *>(dst) =
+            f32x4{ts[0].o[0][rr], ts[0].o[1][rr], ts[0].o[2][rr], ts[0].o[3][rr]};
+        *reinterpret_cast<f32x4 *>(dst + 4) =
+            f32x4{ts[0].o[4][rr], ts[0].o[5][rr], ts[0].o[6][rr], ts[0].o[7][rr]};
+      }
+    }
+    __syncthreads();
+    // merge the 4 waves: thread -> (head h, dims d4..d4+3)
+    const int h = tid >> 4, d4 = (tid & 15) * 4;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) M = fmaxf(M, sm_m[w][h]);
+    f32x4 o = {0.f, 0.f, 0.f, 0.f};
+    float lt = 0.0f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < WAVES; ++w) {
+        const float sc = __builtin_amdgcn_exp2f(sm_m[w][h] - M);
+        lt += sc * sm_l[w][h];
+        o += sc * *reinterpret_cast<const f32x4 *>(&sm_o[w][h][d4]);
+      }
+    }
+    const size_t slot = ((size_t)b * HQ + h) * a.nsplit + s;   // token t = b (L = 1)
+    *reinterpret_cast<f32x4 *>(a.part_o + slot * D + d4) = o;
+    if ((tid & 15) == 0) {
+      a.part_ml[slot * 2] = M;
+      a.part_ml[slot * 2 + 1] = lt;
+    }
+  } else {
+#pragma unroll
+    for (int tk = 0; tk < NT; ++tk) {
+      const float lsum = head_sum(ts[tk].l);
+      if (!ts[tk].live) continue;
+      const int t = b * a.L + wave + WAVES * tk;
+      const size_t slot = ((size_t)t * HQ + n) * a.nsplit + s;
+      if (j == 0) {
+        a.part_ml[slot * 2] = ts[tk].m;
+        a.part_ml[slot * 2 + 1] = lsum;
+      }
+      if (own) {
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          float *dst = a.part_o + slot * D + dbase + 8 * rr;
+          *reinterpret_cast<f32x4 *>(dst) =
+              f32x4{ts[tk].o[0][rr], ts[tk].o[1][rr], ts[tk].o[2][rr], ts[tk].o[3][rr]};
+          *reinterpret_cast<f32x4 *>(dst + 4) =
+              f32x4{ts[tk].o[4][rr], ts[tk].o[5][rr], ts[tk].o[6][rr], ts[tk].o[7][rr]};
+        }
+      }
+    }
+  }
+}
+
+void launch_attn(const StepArgs &a, hipStream_t stream) {
+  const dim3 grid(a.nsplit, a.B), block(256);
+  if (a.L == 1)
+    hipLaunchKernelGGL((attn_splitk_kernel<0, 1, 3>), grid, block, 0, stream, a);
+  else if (a.L <= WAVES)
+    hipLaunchKernelGGL((attn_splitk_kernel<1, 1, 2>), grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL((attn_splitk_kernel<1, 2, 2>), grid, block, 0, stream, a);
+}
+
+}  // namespace museattn

@@ -1,0 +1,100 @@
+// Shared definitions of the gfx950 kernels of libmuseattn.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace museattn {
+
+constexpr int HQ = 16;       // query heads per shard
+constexpr int HKV = 2;       // KV heads per shard
+constexpr int D = 64;        // head dim
+constexpr int GROUP = 8;     // query heads per KV head; head h reads KV head h / 8
+constexpr int QKV_W = 2304;  // fused row: [q 16x64 | k 2x64 | v 2x64 | gate 16x64]
+constexpr int K_OFF = 1024, V_OFF = 1152, G_OFF = 1280;
+constexpr int ROW = 128;     // bytes of one cache row (2 KV heads x 64 E4M3 bytes)
+constexpr int WINDOW = 2048; // sliding window, the query's own position included
+constexpr int CHUNK = 32;    // keys per step of the attention kernel's inner loop
+constexpr int WAVES = 4;     // waves per attention work-group
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Everything one step's kernels read, passed by value.
+struct StepArgs {
+  const uint16_t *qkv;     // bf16 bits [T][2304]
+  const int32_t *positions;
+  const int32_t *table;
+  const int32_t *seq_lens;
+  uint8_t *k_cache;
+  uint8_t *v_cache;
+  uint16_t *out;           // bf16 bits [T][1024]
+  const float *wq, *wk, *wo;
+  float *qbuf;             // [T][16][64] normed, rotated, scaled q
+  float *part_ml;          // [T][16][nsplit][2]  (running max in log2 units, sum)
+  float *part_o;           // [T][16][nsplit][64] unnormalised partial outputs
+  int64_t num_rows;
+  float kv_scale, eps, q_scale, rope_base;
+  int B, L, table_stride, max_seq_len, page_size, sliding;
+  int nsplit, split_keys;
+};
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t h) {
+  return __uint_as_float(((uint32_t)h) << 16);
+}
+
+// Round-to-nearest-even fp32 -> bf16 bits (gfx950 v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
+  __bf16 b = (__bf16)x;
+  return __builtin_bit_cast(uint16_t, b);
+}
+
+// Cache row of request b's key position u (u already clamped into the valid
+// key range).  Page (or row) ids are clamped into the pool so that no table
+// value can address memory outside it.
+__device__ __forceinline__ uint32_t cache_row(const StepArgs &a, int b, int u) {
+  const int ps = a.page_size;
+  const uint32_t units = (uint32_t)(a.num_rows / ps);
+  uint32_t unit = (uint32_t)a.table[(int64_t)b * a.table_stride + u / ps];
+  unit = unit < units ? unit : units - 1;
+  return unit * (uint32_t)ps + (uint32_t)(u % ps);
+}
+
+// The union key range of request b's block tokens.  khi = seq_len - 1; klo =
+// 0 on full layers, first token's position - 2047 on sliding ones.  kbase is
+// klo rounded down to a whole CHUNK.
+struct KeyRange {
+  int klo, khi, kbase;
+};
+
+__device__ __forceinline__ KeyRange request_range(const StepArgs &a, int b) {
+  int sl = a.seq_lens[b];
+  sl = sl < 0 ? 0 : (sl > a.max_seq_len ? a.max_seq_len : sl);
+  KeyRange r;
+  r.khi = sl - 1;
+  r.klo = 0;
+  if (a.sliding) {
+    int p0 = a.positions[b * a.L];
+    p0 = p0 < 0 ? 0 : (p0 > a.max_seq_len - 1 ? a.max_seq_len - 1 : p0);
+    r.klo = p0 - (WINDOW - 1);
+    r.klo = r.klo < 0 ? 0 : r.klo;
+  }
+  r.kbase = r.klo & ~(CHUNK - 1);
+  return r;
+}
+
+// Splits of the key axis that hold keys of request b (the others are idle).
+__device__ __forceinline__ int valid_splits(const StepArgs &a, const KeyRange &r) {
+  if (r.khi < r.klo) return 0;
+  int n = (r.khi + 1 - r.kbase + a.split_keys - 1) / a.split_keys;
+  return n < a.nsplit ? n : a.nsplit;
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
+  return x;
+}
+
+}  // namespace museattn

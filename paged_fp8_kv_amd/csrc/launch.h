@@ -1,0 +1,10 @@
+// Host-side launchers of the step's kernels (each defined next to its kernel).
+#pragma once
+
+#include "device_common.h"
+
+namespace museattn {
+void launch_prologue(const StepArgs &a, hipStream_t stream);
+void launch_attn(const StepArgs &a, hipStream_t stream);
+void launch_combine(const StepArgs &a, hipStream_t stream);
+}  // namespace museattn

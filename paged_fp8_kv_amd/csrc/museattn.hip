@@ -1,0 +1,201 @@
+// Host side of libmuseattn: argument validation, the split schedule (a function
+// of host shapes only, so a call can be captured into a HIP graph), workspace
+// layout and the three launches.  See include/museattn.h for the contract.
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/museattn.h"
+#include "device_common.h"
+#include "launch.h"
+
+namespace museattn {
+namespace {
+
+constexpr int MAX_SPLIT = 4096;     // table entries one work-group caches in LDS
+constexpr int MAX_B = 65535;        // grid.y limit
+constexpr int MAX_SEQ = 1 << 30;
+
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+// Upper bound of one request's key span (from the first block token's window
+// start, rounded down to a chunk, to the last key).
+int64_t span_max(int L, int max_seq_len, int layer_kind) {
+  if (layer_kind == MUSEATTN_SLIDING) {
+    const int64_t s = (int64_t)L + WINDOW - 1 + (CHUNK - 1);
+    return s < max_seq_len ? s : max_seq_len;
+  }
+  return max_seq_len;
+}
+
+int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+// Keys per work-group.  Decode aims at ~2048 work-groups (8 per CU) so the
+// last wave of work-groups is short; verify blocks do 8x the work per key, so
+// they aim at ~256 larger splits to keep the partials small.
+int choose_split(int B, int L, int max_seq_len, int layer_kind, int requested) {
+  if (requested > 0) return requested;
+  const int64_t work = (int64_t)B * span_max(L, max_seq_len, layer_kind);
+  int64_t s;
+  if (L == 1) {
+    s = round_up((work + 2047) / 2048, 128);
+    s = s < 128 ? 128 : s;
+  } else {
+    s = round_up((work + 255) / 256, CHUNK);
+    s = s < 64 ? 64 : s;
+  }
+  return (int)(s > MAX_SPLIT ? MAX_SPLIT : s);
+}
+
+bool split_ok(int split) { return split >= CHUNK && split <= MAX_SPLIT && split % CHUNK == 0; }
+
+struct Layout {
+  int split, nsplit;
+  size_t q_off, ml_off, o_off, total;
+};
+
+Layout layout(int B, int L, int max_seq_len, int layer_kind, int split) {
+  Layout ly;
+  ly.split = split;
+  const int64_t span = span_max(L, max_seq_len, layer_kind);
+  ly.nsplit = (int)((span + split - 1) / split);
+  const size_t T = (size_t)B * L;
+  auto al = [](size_t x) { return (x + 255) / 256 * 256; };
+  ly.q_off = 0;
+  ly.ml_off = al(T * HQ * D * sizeof(float));
+  ly.o_off = ly.ml_off + al(T * HQ * (size_t)ly.nsplit * 2 * sizeof(float));
+  ly.total = ly.o_off + al(T * HQ * (size_t)ly.nsplit * D * sizeof(float));
+  return ly;
+}
+
+int check_shapes(int B, int L, int max_seq_len, int page_size, int layer_kind,
+                 const museattn_params *params) {
+  if (page_size != 1 && page_size != 64) return MUSEATTN_ERR_PAGE_SIZE;
+  if (layer_kind != MUSEATTN_FULL && layer_kind != MUSEATTN_SLIDING) return MUSEATTN_ERR_LAYER_KIND;
+  if (B < 1 || B > MAX_B || L < 1 || L > 8 || max_seq_len < L || max_seq_len > MAX_SEQ)
+    return MUSEATTN_ERR_SHAPE;
+  if (params == nullptr) return MUSEATTN_ERR_NULL;
+  if (params->split_keys != 0 && !split_ok(params->split_keys)) return MUSEATTN_ERR_PARAM;
+  return MUSEATTN_OK;
+}
+
+}  // namespace
+}  // namespace museattn
+
+using namespace museattn;
+
+extern "C" {
+
+int museattn_abi_version(void) { return MUSEATTN_ABI_VERSION; }
+
+const char *museattn_strerror(int status) {
+  switch (status) {
+    case MUSEATTN_OK: return "ok";
+    case MUSEATTN_ERR_NULL: return "a required pointer is null";
+    case MUSEATTN_ERR_PAGE_SIZE: return "page_size must be 1 or 64";
+    case MUSEATTN_ERR_LAYER_KIND: return "layer_kind must be MUSEATTN_FULL or MUSEATTN_SLIDING";
+    case MUSEATTN_ERR_SHAPE: return "B, L, max_seq_len or num_rows out of range";
+    case MUSEATTN_ERR_TABLE: return "table_stride < ceil(max_seq_len / page_size)";
+    case MUSEATTN_ERR_ALIGN: return "misaligned pointer (caches need 16-byte alignment)";
+    case MUSEATTN_ERR_WORKSPACE: return "workspace too small or not 256-byte aligned";
+    case MUSEATTN_ERR_PARAM: return "kv_scale, eps, q_scale, rope_base or split_keys out of range";
+    case MUSEATTN_ERR_ALIAS: return "out overlaps qkv";
+    case MUSEATTN_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int museattn_split_keys(int B, int L, int max_seq_len, int layer_kind, const museattn_params *params) {
+  if (check_shapes(B, L, max_seq_len, 1, layer_kind, params) != MUSEATTN_OK) return 0;
+  return choose_split(B, L, max_seq_len, layer_kind, params->split_keys);
+}
+
+size_t museattn_workspace_bytes(int B, int L, int max_seq_len, int page_size, int layer_kind,
+                                const museattn_params *params) {
+  if (check_shapes(B, L, max_seq_len, page_size, layer_kind, params) != MUSEATTN_OK) return 0;
+  const int split = choose_split(B, L, max_seq_len, layer_kind, params->split_keys);
+  return layout(B, L, max_seq_len, layer_kind, split).total;
+}
+
+int museattn_check_args(const void *qkv, const int32_t *positions, const int32_t *table,
+                        const int32_t *seq_lens, const void *k_cache, const void *v_cache,
+                        float kv_scale, int page_size, int layer_kind, const void *out, int B,
+                        int L, int table_stride, int max_seq_len, int64_t num_rows,
+                        const museattn_params *params, const void *workspace,
+                        size_t workspace_bytes) {
+  if (!qkv || !positions || !table || !seq_lens || !k_cache || !v_cache || !out || !params ||
+      !workspace)
+    return MUSEATTN_ERR_NULL;
+  if (!params->q_norm_w || !params->k_norm_w || !params->o_norm_w) return MUSEATTN_ERR_NULL;
+  const int st = check_shapes(B, L, max_seq_len, page_size, layer_kind, params);
+  if (st != MUSEATTN_OK) return st;
+  if (num_rows < page_size || num_rows % page_size != 0 || num_rows > (int64_t(1) << 32))
+    return MUSEATTN_ERR_SHAPE;
+  if ((int64_t)table_stride * page_size < max_seq_len || table_stride < 1) return MUSEATTN_ERR_TABLE;
+  if (!aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(qkv, 2) || !aligned(out, 2) ||
+      !aligned(positions, 4) || !aligned(table, 4) || !aligned(seq_lens, 4) ||
+      !aligned(params->q_norm_w, 4) || !aligned(params->k_norm_w, 4) ||
+      !aligned(params->o_norm_w, 4))
+    return MUSEATTN_ERR_ALIGN;
+  if (!(std::isfinite(kv_scale) && kv_scale > 0.0f) ||
+      !(std::isfinite(params->eps) && params->eps >= 0.0f) || !std::isfinite(params->q_scale) ||
+      !(std::isfinite(params->rope_base) && params->rope_base > 0.0f))
+    return MUSEATTN_ERR_PARAM;
+  if (!aligned(workspace, 256) ||
+      workspace_bytes < museattn_workspace_bytes(B, L, max_seq_len, page_size, layer_kind, params))
+    return MUSEATTN_ERR_WORKSPACE;
+  const uintptr_t q0 = (uintptr_t)qkv, q1 = q0 + (uintptr_t)B * L * QKV_W * 2;
+  const uintptr_t o0 = (uintptr_t)out, o1 = o0 + (uintptr_t)B * L * HQ * D * 2;
+  if (o0 < q1 && q0 < o1) return MUSEATTN_ERR_ALIAS;
+  return MUSEATTN_OK;
+}
+
+int museattn_attn_step(const void *qkv, const int32_t *positions, const int32_t *table,
+                       const int32_t *seq_lens, void *k_cache, void *v_cache, float kv_scale,
+                       int page_size, int layer_kind, void *out, void *stream, int B, int L,
+                       int table_stride, int max_seq_len, int64_t num_rows,
+                       const museattn_params *params, void *workspace, size_t workspace_bytes) {
+  const int st = museattn_check_args(qkv, positions, table, seq_lens, k_cache, v_cache, kv_scale,
+                                     page_size, layer_kind, out, B, L, table_stride, max_seq_len,
+                                     num_rows, params, workspace, workspace_bytes);
+  if (st != MUSEATTN_OK) return st;
+  const int split = choose_split(B, L, max_seq_len, layer_kind, params->split_keys);
+  const Layout ly = layout(B, L, max_seq_len, layer_kind, split);
+  char *ws = static_cast<char *>(workspace);
+
+  StepArgs a;
+  a.qkv = static_cast<const uint16_t *>(qkv);
+  a.positions = positions;
+  a.table = table;
+  a.seq_lens = seq_lens;
+  a.k_cache = static_cast<uint8_t *>(k_cache);
+  a.v_cache = static_cast<uint8_t *>(v_cache);
+  a.out = static_cast<uint16_t *>(out);
+  a.wq = params->q_norm_w;
+  a.wk = params->k_norm_w;
+  a.wo = params->o_norm_w;
+  a.qbuf = reinterpret_cast<float *>(ws + ly.q_off);
+  a.part_ml = reinterpret_cast<float *>(ws + ly.ml_off);
+  a.part_o = reinterpret_cast<float *>(ws + ly.o_off);
+  a.num_rows = num_rows;
+  a.kv_scale = kv_scale;
+  a.eps = params->eps;
+  a.q_scale = params->q_scale;
+  a.rope_base = params->rope_base;
+  a.B = B;
+  a.L = L;
+  a.table_stride = table_stride;
+  a.max_seq_len = max_seq_len;
+  a.page_size = page_size;
+  a.sliding = layer_kind == MUSEATTN_SLIDING;
+  a.nsplit = ly.nsplit;
+  a.split_keys = ly.split;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();   // clear an error left by earlier, unrelated calls
+  launch_prologue(a, s);
+  launch_attn(a, s);
+  launch_combine(a, s);
+  return hipGetLastError() == hipSuccess ? MUSEATTN_OK : MUSEATTN_ERR_LAUNCH;
+}
+
+}  // extern "C"

@@ -45,6 +45,7 @@ class Workload:
     w_o: np.ndarray
     table: np.ndarray        # int32 [B, table_stride]; unused slots = -1
     pages: list = field(default_factory=list)  # per request: int64 page (or row) ids in order
+    origin: list = field(default_factory=list)  # request ids in the workload drawn (subsets)
 
     @property
     def T(self) -> int:
@@ -76,10 +77,23 @@ class Workload:
             span = self.seq_lens.astype(np.int64) - lo
         return int(span.sum()) * 2 * ROW_BYTES
 
+    def subset(self, requests) -> "Workload":
+        """The same draws restricted to some requests (their pool placement kept)."""
+        req = [int(b) for b in requests]
+        sub = Workload(name=f"{self.name}[{len(req)} of {self.B}]", seed=self.seed, B=len(req),
+                       L=self.L, layer_kind=self.layer_kind, page_size=self.page_size,
+                       kv_scale=self.kv_scale, ctx=self.ctx[req].copy(), num_rows=self.num_rows,
+                       qkv=self.qkv.view(self.B, self.L, QKV_WIDTH)[req].reshape(-1, QKV_WIDTH).clone(),
+                       w_q=self.w_q, w_k=self.w_k, w_o=self.w_o, table=self.table[req].copy(),
+                       pages=[self.pages[b] for b in req],
+                       origin=[self.origin[b] if self.origin else b for b in req])
+        return sub
+
     def cache_values(self, b: int) -> tuple[np.ndarray, np.ndarray]:
         """Bytes of request b's cached positions 0..ctx_b-1: K, V uint8 [ctx_b, 2, 64]."""
         n = int(self.ctx[b])
-        rng = np.random.Generator(np.random.PCG64([self.seed, b]))
+        src = self.origin[b] if self.origin else b
+        rng = np.random.Generator(np.random.PCG64([self.seed, src]))
         x = rng.standard_normal(2 * n * ROW_BYTES, dtype=np.float32)
         np.clip(x, -_CLIP, _CLIP, out=x)
         xt = torch.from_numpy(x)

@@ -1,0 +1,124 @@
+"""The C ABI on the host: the library loads, exports every symbol the header
+declares, and its argument validation returns the documented statuses
+without touching a device (fake, aligned pointer values)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import paged_fp8_kv_amd as P
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "museattn.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(museattn_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = P.lib()
+    names = _declared()
+    assert set(names) == set(P.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert P.abi_version() == 1
+
+
+def test_strerror_covers_all_statuses():
+    for st in P.STATUS:
+        assert P.strerror(st) and P.strerror(st) != "unknown status"
+    assert P.strerror(12345) == "unknown status"
+
+
+# fake device addresses: far apart, 256-byte aligned
+BASE = 1 << 40
+A = {k: BASE + i * (1 << 34) for i, k in enumerate(
+    ["qkv", "pos", "table", "seq", "kc", "vc", "out", "ws", "wq", "wk", "wo"])}
+
+
+def _args(**kw):
+    B, L, msl, ps, kind = kw.get("B", 4), kw.get("L", 1), kw.get("max_seq_len", 1000), \
+        kw.get("page_size", 1), kw.get("layer_kind", P.FULL)
+    params = P.make_params(kw.get("wq", A["wq"]), A["wk"], A["wo"], kw.get("eps", 1e-6),
+                           kw.get("q_scale", 5.473), kw.get("rope_base", 1e4),
+                           kw.get("split_keys", 0))
+    need = P.lib().museattn_workspace_bytes(B, L, msl, ps if ps in (1, 64) else 1,
+                                            kind if kind in (0, 1) else 0, ctypes.byref(params))
+    return dict(qkv=kw.get("qkv", A["qkv"]), positions=A["pos"], table=A["table"],
+                seq_lens=A["seq"], k_cache=kw.get("kc", A["kc"]), v_cache=A["vc"],
+                kv_scale=kw.get("kv_scale", 1.0), page_size=ps, layer_kind=kind,
+                out=kw.get("out", A["out"]), B=B, L=L,
+                table_stride=kw.get("table_stride", 1000), max_seq_len=msl,
+                num_rows=kw.get("num_rows", 1 << 20), params=params,
+                workspace=kw.get("ws", A["ws"]), workspace_nbytes=kw.get("ws_bytes", need))
+
+
+def _check(**kw):
+    return P.check_args(**_args(**kw))
+
+
+def test_valid_arguments_pass():
+    assert _check() == 0
+    assert _check(page_size=64, table_stride=16, num_rows=64 * 100) == 0
+    assert _check(L=8, layer_kind=P.SLIDING) == 0
+    assert _check(split_keys=4096) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(qkv=0), -1),
+    (dict(wq=0), -1),
+    (dict(ws=0), -1),
+    (dict(page_size=16), -2),
+    (dict(layer_kind=2), -3),
+    (dict(L=9), -4),
+    (dict(L=0), -4),
+    (dict(B=0), -4),
+    (dict(B=70000), -4),
+    (dict(max_seq_len=0), -4),
+    (dict(num_rows=0), -4),
+    (dict(page_size=64, table_stride=100, num_rows=1000), -4),   # not a multiple of 64
+    (dict(table_stride=999), -5),
+    (dict(page_size=64, table_stride=15, num_rows=6400), -5),
+    (dict(kc=A["kc"] + 8), -6),
+    (dict(qkv=A["qkv"] + 1), -6),
+    (dict(ws_bytes=1024), -7),
+    (dict(ws=A["ws"] + 128), -7),
+    (dict(kv_scale=0.0), -8),
+    (dict(kv_scale=float("nan")), -8),
+    (dict(eps=-1.0), -8),
+    (dict(rope_base=0.0), -8),
+    (dict(split_keys=100), -8),
+    (dict(split_keys=8192), -8),
+    (dict(out=A["qkv"] + 4096), -9),
+])
+def test_invalid_arguments_are_rejected(kw, status):
+    assert _check(**kw) == status
+
+
+def test_workspace_and_split_schedule():
+    # decode at the large batch: ~2048 work-groups, splits multiple of 128
+    sk = P.split_keys(32, 1, 100001, P.FULL)
+    assert sk % 128 == 0 and 1024 <= sk <= 4096
+    n = P.workspace_bytes(32, 1, 100001, 1, P.FULL)
+    nsplit = -(-100001 // sk)
+    assert n >= 32 * 16 * 64 * 4 + 32 * 16 * nsplit * 66 * 4
+    # the sliding span is bounded by the window whatever the context
+    assert P.workspace_bytes(4, 8, 1 << 20, 1, P.SLIDING) == P.workspace_bytes(4, 8, 4096, 1, P.SLIDING)
+    with pytest.raises(ValueError):
+        P.workspace_bytes(1, 9, 100, 1, P.FULL)
+
+
+def test_attn_step_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros(1, 2304, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        P.attn_step(x, torch.zeros(1, dtype=torch.int32), torch.zeros(1, 1, dtype=torch.int32),
+                    torch.ones(1, dtype=torch.int32), torch.zeros(128, dtype=torch.uint8),
+                    torch.zeros(128, dtype=torch.uint8), 1.0, 1, P.FULL,
+                    torch.zeros(1, 1, 1024, dtype=torch.bfloat16),
+                    q_norm_w=torch.ones(64), k_norm_w=torch.ones(64), o_norm_w=torch.ones(64),
+                    max_seq_len=1)

@@ -1,0 +1,206 @@
+"""GPU parity: the HIP step through the C ABI against the CPU oracle.
+
+Bar: every written cache byte within 1 E4M3 ulp of the oracle's (v bytes exact
+for power-of-two kv_scale); the oracle, attending to the GPU's own new
+entries, matches the bf16 output within max-abs 2e-2 and mean-abs 2e-3.
+"""
+import numpy as np
+import pytest
+import torch
+
+import paged_fp8_kv_amd as P
+from oracle import museattn_oracle as O
+from paged_fp8_kv_amd import workloads as W
+
+from gpu_common import full_check, gpu_new_bytes, log, new_rows, oracle_prologue, run, upload
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    P.lib()   # raises if the HIP library is missing
+
+
+def _untouched_rows_kept(w, d, host):
+    """Every row other than the new tokens' rows still holds its old bytes."""
+    rows = new_rows(w)
+    for dev_pool, host_pool in ((d["k_cache"], host[0]), (d["v_cache"], host[1])):
+        got = dev_pool.cpu().numpy()
+        keep = np.ones(w.num_rows, bool)
+        keep[rows] = False
+        assert np.array_equal(got[keep], host_pool[keep]), "a row outside the new tokens changed"
+
+
+# ------------------------------------------------ the workloads of record
+
+@pytest.mark.parametrize("cid", ["0", "1", "3s", "3f"])
+def test_config_parity(cid):
+    w = W.config(cid)
+    log(f"[config {cid}] {w.name} B={w.B} L={w.L} ctx={w.ctx.tolist()[:4]} ps={w.page_size}")
+    host = W.build_pools_numpy(w)
+    d = upload(w)
+    run(w, d)
+    torch.cuda.synchronize()
+    full_check(w, d, host_pools=host)
+    _untouched_rows_kept(w, d, host)
+
+
+@pytest.mark.parametrize("cid,requests", [("2", [0, 9, 17, 31]), ("4", [0, 5, 15])])
+def test_config_parity_full_size_sampled(cid, requests):
+    """Full-size pools and batch in the launch configuration the bench times;
+    the oracle recomputes a sample of requests (with the shortest and longest
+    contexts among them)."""
+    w = W.config(cid)
+    req = sorted(set(requests) | {int(np.argmin(w.ctx)), int(np.argmax(w.ctx))})
+    log(f"[config {cid}] {w.name} B={w.B} pool rows={w.num_rows} checking {req}")
+    d = upload(w)
+    run(w, d)
+    torch.cuda.synchronize()
+    full_check(w, d, requests=req)
+    # the other requests: finite output, bytes within 1 ulp (checked inside for all)
+    assert torch.isfinite(d["out"].float()).all()
+    del d
+    torch.cuda.empty_cache()
+
+
+# ---------------------------------------------- edge cases and page's tests
+
+EDGE = [
+    # name, B, L, ctx, kind, page_size, kv_scale
+    ("empty-context", 2, 1, 0, W.FULL, 1, 1.0),
+    ("ctx10-sliding", 1, 1, 10, W.SLIDING, 64, 1.0),
+    ("ctx2047-sliding-b3", 3, 1, 2047, W.SLIDING, 64, 1.0),
+    ("b5-L8-sliding-spread", 5, 8, (4000, 6000), W.SLIDING, 1, 1.0),
+    ("b4-full-ctx3000-p64", 4, 1, 3000, W.FULL, 64, 1.0),
+    ("b4-L8-sliding-window-edges", 4, 8, (2038, 2058), W.SLIDING, 1, 1.0),
+    ("b4-L8-full-ctx6000", 4, 8, 6000, W.FULL, 64, 1.0),
+    ("b3-L8-sliding-kv1/64-p1", 3, 8, 4000, W.SLIDING, 1, 1.0 / 64),
+    ("b2-full-kv1/64-p64", 2, 1, 9000, W.FULL, 64, 1.0 / 64),
+    ("b2-L8-full-ctx20000-p64", 2, 8, 20000, W.FULL, 64, 1.0),
+    ("b3-L2-full", 3, 2, (100, 700), W.FULL, 64, 1.0),
+    ("b2-L3-sliding", 2, 3, (2500, 3000), W.SLIDING, 1, 1.0),
+    ("b2-L5-full", 2, 5, (900, 1300), W.FULL, 1, 1.0),
+    ("b2-L7-sliding", 2, 7, (3000, 3100), W.SLIDING, 64, 1.0),
+    ("b33-full-spread", 33, 1, (15000, 25000), W.FULL, 1, 1.0),
+    ("b2-full-kv0.3", 2, 1, 500, W.FULL, 1, 0.3),
+    ("b1-L8-ragged-tail", 1, 8, 4125, W.FULL, 1, 1.0),
+]
+
+
+@pytest.mark.parametrize("case", EDGE, ids=[c[0] for c in EDGE])
+def test_edge_parity(case):
+    name, B, L, ctx, kind, ps, kv = case
+    w = W.make(name, 77, B, L, ctx, kind, ps, kv)
+    log(f"[edge] {name} ctx={w.ctx.tolist()[:6]} split={P.split_keys(B, L, w.max_seq_len, kind)}")
+    host = W.build_pools_numpy(w)
+    d = upload(w)
+    run(w, d)
+    torch.cuda.synchronize()
+    full_check(w, d, host_pools=host)
+    _untouched_rows_kept(w, d, host)
+
+
+@pytest.mark.slow
+def test_million_key_verify_block():
+    """A full layer over 1,048,576 cached keys with an 8-token block."""
+    w = W.make("ctx1M-L8-full", 91, 1, 8, 1048576, W.FULL, 1, 1.0)
+    log(f"[edge] {w.name}")
+    d = upload(w)
+    run(w, d)
+    torch.cuda.synchronize()
+    full_check(w, d, requests=[0])
+
+
+# ----------------------------------------------------------- properties
+
+def test_split_count_invariance_and_determinism():
+    w = W.make("splits", 5, 3, 1, (3000, 9000), W.FULL, 1, 1.0)
+    host = W.build_pools_numpy(w)
+    d = upload(w)
+    outs = []
+    for sk in (32, 128, 320, 1024, 4096, 0):
+        log(f"[split] split_keys={sk}")
+        run(w, d, split_keys=sk)
+        outs.append(d["out"].clone())
+    torch.cuda.synchronize()
+    full_check(w, d, host_pools=host)
+    ref = outs[-1].float()
+    for o in outs[:-1]:
+        assert (o.float() - ref).abs().max().item() <= 1.6e-2
+    run(w, d)
+    assert torch.equal(d["out"], outs[-1]), "two identical calls differ"
+
+
+def test_verify_split_invariance():
+    w = W.make("vsplits", 6, 2, 8, (2500, 4000), W.SLIDING, 1, 1.0)
+    host = W.build_pools_numpy(w)
+    d = upload(w)
+    outs = []
+    for sk in (32, 96, 1024, 0):
+        run(w, d, split_keys=sk)
+        outs.append(d["out"].clone())
+    torch.cuda.synchronize()
+    full_check(w, d, host_pools=host)
+    for o in outs[:-1]:
+        assert (o.float() - outs[-1].float()).abs().max().item() <= 1.6e-2
+
+
+def test_page_size_does_not_change_the_result():
+    outs = []
+    for ps in (1, 64):
+        w = W.make("ps", 12, 4, 8, (700, 1500), W.FULL, ps, 1.0)
+        d = upload(w)
+        run(w, d)
+        outs.append(d["out"].clone())
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1])
+
+
+def test_value_encoder_exhaustive_over_bf16():
+    """v goes to the cache unnormed, so every finite bf16 value (and +-inf) is
+    fed to the fp8 encoder; with kv_scale 1 the bytes must equal the oracle's
+    exactly (ties to even, subnormals, saturation at +-448)."""
+    bits = np.arange(65536, dtype=np.uint32)
+    vals = (bits << 16).view(np.float32).copy()
+    vals[np.isnan(vals)] = 1.0
+    w = W.make("v-encoder", 3, 64, 8, 4, W.FULL, 1, 1.0)
+    qkv = w.qkv.clone()
+    qkv[:, 1152:1280] = torch.from_numpy(vals).to(torch.bfloat16).view(512, 128)
+    w.qkv = qkv
+    d = upload(w)
+    run(w, d)
+    torch.cuda.synchronize()
+    _, vb_gpu = gpu_new_bytes(w, d)
+    _, _, vb, _ = oracle_prologue(w)
+    assert np.array_equal(vb_gpu, vb)
+
+
+def test_graph_capture_replays_match_eager():
+    w = W.make("graph", 8, 4, 1, (2000, 5000), W.FULL, 1, 1.0)
+    d = upload(w)
+    ws = torch.empty(P.workspace_bytes(w.B, w.L, w.max_seq_len, w.page_size, w.layer_kind),
+                     dtype=torch.uint8, device="cuda:0")
+    run(w, d, workspace=ws)
+    torch.cuda.synchronize()
+    eager = d["out"].clone()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        run(w, d, workspace=ws)     # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        run(w, d, workspace=ws)
+    for i in range(3):
+        d["out"].zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(d["out"], eager), f"replay {i} differs from the eager call"
+        run(w, d, workspace=ws)     # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(d["out"], eager)
