@@ -1,0 +1,261 @@
+"""Benchmark of the attention step on one MI355X.
+
+Default workload: decode, batch 32, full-attention layer, per-request
+context drawn uniformly from [60000, 100000] (seed 1002), page size 1, random
+cache rows in ~80 GB of K+V pools, kv_scale 1.  A step is one museattn_attn_step
+call (prologue, split-K attention, combine) over that batch with every input
+already resident in HBM.
+
+Prints ONE JSON line on stdout (progress goes to stderr):
+  value       achieved HBM throughput of the step on the algorithmic K+V bytes
+              (256 B per visible key), GB/s
+  roofline    the split-K attention kernel alone, timed with HIP events on the
+              stream it runs on, against MI355X's 8 TB/s
+  cpu_baseline  the CPU oracle on a sample of the same workload
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "attn_splitk_decode_b32_full_ctx80k_pmc.txt")
+ATTN_SOURCE = os.path.join(ROOT, "paged_fp8_kv_amd", "csrc", "attn_splitk.hip")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def hip_elapsed_ms(start, end) -> float:
+    """hipEventElapsedTime on the raw handles of two torch events (recorded by
+    the library, so torch's own bookkeeping does not know they were recorded)."""
+    import ctypes
+    global _HIP
+    if "_HIP" not in globals():
+        _HIP = ctypes.CDLL("libamdhip64.so")
+        _HIP.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                             ctypes.c_void_p]
+        _HIP.hipEventElapsedTime.restype = ctypes.c_int
+    ms = ctypes.c_float()
+    st = _HIP.hipEventElapsedTime(ctypes.byref(ms), start.cuda_event, end.cuda_event)
+    if st != 0:
+        raise RuntimeError(f"hipEventElapsedTime failed with status {st}")
+    return ms.value
+
+
+def kernel_source_hash() -> str:
+    with open(ATTN_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def read_traffic(bytes_per_launch_alg):
+    """HBM bytes per launch of the attention kernel from the committed PMC
+    summary (FETCH_SIZE + WRITE_SIZE, scaled by a copy-kernel calibration), or
+    None when the summary is absent or was taken on another kernel source."""
+    if not os.path.exists(PMC_SUMMARY):
+        return None
+    vals = {}
+    with open(PMC_SUMMARY) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(w, sample_requests: int):
+    """The oracle (as it stands) on a sample of the workload's requests."""
+    import numpy as np
+    from oracle import museattn_oracle as O
+    from paged_fp8_kv_amd import workloads as W
+
+    req = list(range(min(sample_requests, w.B)))
+    sub = w.subset(req)
+    log(f"cpu_baseline: building the oracle's view of requests {req[0]}..{req[-1]}")
+    kp = W.LogicalPool(sub, range(sub.B), "k")
+    vp = W.LogicalPool(sub, range(sub.B), "v")
+    threads = 1
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        pass
+    t0 = time.perf_counter()
+    O.attn_step(sub.qkv.float().numpy(), sub.positions, sub.table, kp, vp, B=sub.B, L=sub.L,
+                page_size=sub.page_size, layer_kind=sub.layer_kind, kv_scale=sub.kv_scale,
+                w_q=sub.w_q, w_k=sub.w_k, w_o=sub.w_o, eps=float(np.float32(1e-6)),
+                q_scale=float(np.float32(5.473)))
+    dt = time.perf_counter() - t0
+    frac = sub.kv_bytes / w.kv_bytes
+    step_s = dt / frac
+    log(f"cpu_baseline: {dt:.2f} s for {sub.kv_bytes / 1e6:.1f} MB of K+V -> {step_s:.2f} s/step")
+    return {"value": round(w.kv_bytes / step_s / 1e9, 4), "unit": "GB/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"requests 0..{req[-1]} ({sub.B} of {w.B}, {frac * 100:.1f}% of the step's "
+                      f"K+V bytes), float64 numpy oracle, {dt:.2f} s; scaled to one step "
+                      f"({step_s:.2f} s/step)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="2", help="workload id (0, 1, 2, 3s, 3f, 4)")
+    ap.add_argument("--split-keys", type=int, default=0)
+    ap.add_argument("--pool-rows", type=int, default=0,
+                    help="override the pool size in rows (0 = the workload's own)")
+    ap.add_argument("--cold-reps", type=int, default=30,
+                    help="graph replays timed one by one after a 1 GiB cache flush")
+    ap.add_argument("--cpu-sample", type=int, default=16, help="requests the oracle times")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibration-copy", action="store_true",
+                    help="run a 1 GiB device copy first (PMC calibration runs)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the "
+              "multi-GPU sharding of the step is described in DESIGN.md, not run.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import paged_fp8_kv_amd as P
+    from paged_fp8_kv_amd import workloads as W
+
+    dev = "cuda:0"
+    P.lib()
+    w = W.config(args.config, args.pool_rows or None)
+    log(f"workload {w.name}: B={w.B} L={w.L} keys={int(w.kv_bytes // 256)} "
+        f"K+V bytes={w.kv_bytes / 1e6:.1f} MB pool rows={w.num_rows}")
+    t0 = time.perf_counter()
+    kp, vp = W.build_pools_device(w, dev)
+    f = lambda a: torch.from_numpy(a.copy()).to(dev)  # noqa: E731
+    d = dict(qkv=w.qkv.to(dev), positions=f(w.positions), table=f(w.table), seq_lens=f(w.seq_lens),
+             w_q=f(w.w_q), w_k=f(w.w_k), w_o=f(w.w_o))
+    out = torch.empty(w.B, w.L, 1024, dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(P.workspace_bytes(w.B, w.L, w.max_seq_len, w.page_size, w.layer_kind,
+                                       args.split_keys), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    log(f"inputs resident in HBM ({time.perf_counter() - t0:.1f} s)")
+
+    if args.calibration_copy:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        a.fill_(1)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+        log("calibration copy of 1 GiB done")
+
+    def step(events=None):
+        P.attn_step(d["qkv"], d["positions"], d["table"], d["seq_lens"], kp, vp, w.kv_scale,
+                    w.page_size, w.layer_kind, out, q_norm_w=d["w_q"], k_norm_w=d["w_k"],
+                    o_norm_w=d["w_o"], max_seq_len=w.max_seq_len, workspace=ws,
+                    split_keys=args.split_keys, attn_events=events)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} steps done")
+
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for pair in evs:        # torch creates the HIP event on its first record
+        for e in pair:
+            e.record()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    attn_ms = [hip_elapsed_ms(s, e) for s, e in evs]
+    attn_avg_ms = sum(attn_ms) / len(attn_ms)
+    log(f"timed {args.steps} steps: {ms_per_step * 1e3:.1f} us/step; attention kernel "
+        f"avg {attn_avg_ms * 1e3:.1f} us (min {min(attn_ms) * 1e3:.1f})")
+
+    cold = None
+    if args.cold_reps > 0:
+        # a read of 1 GiB evicts the step's data from the caches without leaving
+        # dirty lines behind (a write-flush would add write-back traffic)
+        flush = torch.ones(1 << 28, dtype=torch.int32, device=dev)
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            step()
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            step()
+        times = []
+        for _ in range(args.cold_reps):
+            flush.sum()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1) * 1e3)
+        times.sort()
+        cold = {"median_us": round(statistics.median(times), 2),
+                "p10_us": round(times[len(times) // 10], 2),
+                "p90_us": round(times[(len(times) * 9) // 10], 2), "reps": len(times)}
+        log(f"graph replay after a 1 GiB flush: median {cold['median_us']} us "
+            f"(p10 {cold['p10_us']}, p90 {cold['p90_us']})")
+        del flush
+
+    kv = w.kv_bytes
+    value = kv / (ms_per_step * 1e-3) / 1e9
+    achieved = kv / (attn_avg_ms * 1e-3) / 1e9
+    traffic = read_traffic(kv)
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": traffic, "kernel": "attn_splitk_kernel (split-K attention)",
+                "algorithmic_bytes_per_launch": kv, "avg_launch_us": round(attn_avg_ms * 1e3, 2)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, args.cpu_sample)
+
+    line = {
+        "metric": "us/step and achieved HBM GB/s (% peak), decode-32 full-attn ctx 80K, 1 GPU",
+        "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "us_per_step": round(ms_per_step * 1e3, 2), "pct_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "kv_dtype": "fp8_e4m3fn", "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "L": w.L, "layer": "full" if w.layer_kind == 0
+                   else "sliding", "page_size": w.page_size, "kv_scale": w.kv_scale,
+                   "ctx_min": int(w.ctx.min()), "ctx_max": int(w.ctx.max()),
+                   "ctx_mean": round(float(w.ctx.mean()), 1), "keys": int(kv // 256),
+                   "kv_bytes": kv, "pool_rows": w.num_rows, "seed": w.seed,
+                   "split_keys": P.split_keys(w.B, w.L, w.max_seq_len, w.layer_kind,
+                                              args.split_keys)},
+        "cold_cache_graph_replay": cold,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

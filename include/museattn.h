@@ -139,6 +139,19 @@ int museattn_attn_step(const void *qkv, const int32_t *positions, const int32_t 
                        int table_stride, int max_seq_len, int64_t num_rows,
                        const museattn_params *params, void *workspace, size_t workspace_bytes);
 
+/* museattn_attn_step that also records two caller-created hipEvent_t on
+ * `stream`, immediately before and after the split-K attention kernel (the
+ * step's dominant kernel), so a profiler of the caller can time that kernel
+ * alone.  Either event may be NULL (not recorded).  Same arguments, effects
+ * and statuses as museattn_attn_step. */
+int museattn_attn_step_profiled(const void *qkv, const int32_t *positions, const int32_t *table,
+                                const int32_t *seq_lens, void *k_cache, void *v_cache,
+                                float kv_scale, int page_size, int layer_kind, void *out,
+                                void *stream, int B, int L, int table_stride, int max_seq_len,
+                                int64_t num_rows, const museattn_params *params, void *workspace,
+                                size_t workspace_bytes, void *attn_start_event,
+                                void *attn_end_event);
+
 /* Keys per split the library uses for these shapes (split_keys = 0 chooses). */
 int museattn_split_keys(int B, int L, int max_seq_len, int layer_kind, const museattn_params *params);
 

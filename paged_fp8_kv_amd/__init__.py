@@ -31,7 +31,8 @@ STATUS = {
 
 # every symbol include/museattn.h declares
 EXPORTS = ("museattn_abi_version", "museattn_strerror", "museattn_workspace_bytes",
-           "museattn_check_args", "museattn_attn_step", "museattn_split_keys")
+           "museattn_check_args", "museattn_attn_step", "museattn_attn_step_profiled",
+           "museattn_split_keys")
 
 
 class Params(ctypes.Structure):
@@ -79,6 +80,8 @@ def lib() -> ctypes.CDLL:
         L.museattn_attn_step.restype = i32
         L.museattn_attn_step.argtypes = common + [vp, i32, i32, i32, i32, i64, pp, vp,
                                                   ctypes.c_size_t]
+        L.museattn_attn_step_profiled.restype = i32
+        L.museattn_attn_step_profiled.argtypes = L.museattn_attn_step.argtypes + [vp, vp]
         _lib = L
     return _lib
 
@@ -133,7 +136,7 @@ def _need(cond, msg):
 def attn_step(qkv, positions, table, seq_lens, k_cache, v_cache, kv_scale, page_size,
               layer_kind, out, stream=None, *, q_norm_w, k_norm_w, o_norm_w, max_seq_len,
               workspace=None, eps=DEFAULT_EPS, q_scale=DEFAULT_Q_SCALE,
-              rope_base=DEFAULT_ROPE_BASE, split_keys=0):
+              rope_base=DEFAULT_ROPE_BASE, split_keys=0, attn_events=None):
     """One attention step on torch tensors (see include/museattn.h).
 
     qkv bf16 [B*L, 2304]; positions int32 [B*L]; table int32 [B, stride];
@@ -141,7 +144,9 @@ def attn_step(qkv, positions, table, seq_lens, k_cache, v_cache, kv_scale, page_
     uint8 view of that many bytes); out bf16 [B, L, 1024]; norm weights
     float32 [64]; workspace uint8 of >= workspace_bytes(...) bytes or None
     (then allocated here with torch).  stream: a torch.cuda.Stream, a raw
-    hipStream_t int, or None for the current stream."""
+    hipStream_t int, or None for the current stream.  attn_events: optional
+    (start, end) torch.cuda.Event pair recorded around the attention kernel
+    (museattn_attn_step_profiled)."""
     import torch
 
     B = int(seq_lens.shape[0])
@@ -179,12 +184,16 @@ def attn_step(qkv, positions, table, seq_lens, k_cache, v_cache, kv_scale, page_
         stream_ptr = stream.cuda_stream
     else:
         stream_ptr = int(stream)
-    st = lib().museattn_attn_step(qkv.data_ptr(), positions.data_ptr(), table.data_ptr(),
-                                  seq_lens.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
-                                  float(kv_scale), int(page_size), int(layer_kind),
-                                  out.data_ptr(), stream_ptr, B, L, int(table.shape[1]),
-                                  int(max_seq_len), int(num_rows), ctypes.byref(params),
-                                  workspace.data_ptr(), int(workspace.numel()))
+    args = (qkv.data_ptr(), positions.data_ptr(), table.data_ptr(), seq_lens.data_ptr(),
+            k_cache.data_ptr(), v_cache.data_ptr(), float(kv_scale), int(page_size),
+            int(layer_kind), out.data_ptr(), stream_ptr, B, L, int(table.shape[1]),
+            int(max_seq_len), int(num_rows), ctypes.byref(params), workspace.data_ptr(),
+            int(workspace.numel()))
+    if attn_events is None:
+        st = lib().museattn_attn_step(*args)
+    else:
+        st = lib().museattn_attn_step_profiled(*args, attn_events[0].cuda_event,
+                                               attn_events[1].cuda_event)
     if st != OK:
         raise MuseAttnError(st, "museattn_attn_step")
     return out

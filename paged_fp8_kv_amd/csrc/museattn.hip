@@ -149,11 +149,13 @@ int museattn_check_args(const void *qkv, const int32_t *positions, const int32_t
   return MUSEATTN_OK;
 }
 
-int museattn_attn_step(const void *qkv, const int32_t *positions, const int32_t *table,
-                       const int32_t *seq_lens, void *k_cache, void *v_cache, float kv_scale,
-                       int page_size, int layer_kind, void *out, void *stream, int B, int L,
-                       int table_stride, int max_seq_len, int64_t num_rows,
-                       const museattn_params *params, void *workspace, size_t workspace_bytes) {
+int museattn_attn_step_profiled(const void *qkv, const int32_t *positions, const int32_t *table,
+                                const int32_t *seq_lens, void *k_cache, void *v_cache,
+                                float kv_scale, int page_size, int layer_kind, void *out,
+                                void *stream, int B, int L, int table_stride, int max_seq_len,
+                                int64_t num_rows, const museattn_params *params, void *workspace,
+                                size_t workspace_bytes, void *attn_start_event,
+                                void *attn_end_event) {
   const int st = museattn_check_args(qkv, positions, table, seq_lens, k_cache, v_cache, kv_scale,
                                      page_size, layer_kind, out, B, L, table_stride, max_seq_len,
                                      num_rows, params, workspace, workspace_bytes);
@@ -193,9 +195,22 @@ int museattn_attn_step(const void *qkv, const int32_t *positions, const int32_t 
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();   // clear an error left by earlier, unrelated calls
   launch_prologue(a, s);
+  if (attn_start_event) (void)hipEventRecord(static_cast<hipEvent_t>(attn_start_event), s);
   launch_attn(a, s);
+  if (attn_end_event) (void)hipEventRecord(static_cast<hipEvent_t>(attn_end_event), s);
   launch_combine(a, s);
   return hipGetLastError() == hipSuccess ? MUSEATTN_OK : MUSEATTN_ERR_LAUNCH;
+}
+
+int museattn_attn_step(const void *qkv, const int32_t *positions, const int32_t *table,
+                       const int32_t *seq_lens, void *k_cache, void *v_cache, float kv_scale,
+                       int page_size, int layer_kind, void *out, void *stream, int B, int L,
+                       int table_stride, int max_seq_len, int64_t num_rows,
+                       const museattn_params *params, void *workspace, size_t workspace_bytes) {
+  return museattn_attn_step_profiled(qkv, positions, table, seq_lens, k_cache, v_cache, kv_scale,
+                                     page_size, layer_kind, out, stream, B, L, table_stride,
+                                     max_seq_len, num_rows, params, workspace, workspace_bytes,
+                                     nullptr, nullptr);
 }
 
 }  // extern "C"
