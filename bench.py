@@ -3,7 +3,8 @@
 Default workload: decode, batch 32, full-attention layer, per-request
 context drawn uniformly from [60000, 100000] (seed 1002), page size 1, random
 cache rows in ~80 GB of K+V pools, kv_scale 1.  A step is one museattn_attn_step
-call (prologue, split-K attention, combine) over that batch with every input
+call (prologue kernel, then the split-K attention kernel that also merges
+the partials and writes the gated output) over that batch with every input
 already resident in HBM.
 
 Prints ONE JSON line on stdout (progress goes to stderr):
@@ -116,7 +117,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="2", help="workload id (0, 1, 2, 3s, 3f, 4)")
-    ap.add_argument("--split-keys", type=int, default=0)
+    ap.add_argument("--work-groups", type=int, default=0,
+                    help="attention work-groups (0 = the library's choice)")
     ap.add_argument("--pool-rows", type=int, default=0,
                     help="override the pool size in rows (0 = the workload's own)")
     ap.add_argument("--cold-reps", type=int, default=30,
@@ -150,7 +152,7 @@ def main():
              w_q=f(w.w_q), w_k=f(w.w_k), w_o=f(w.w_o))
     out = torch.empty(w.B, w.L, 1024, dtype=torch.bfloat16, device=dev)
     ws = torch.empty(P.workspace_bytes(w.B, w.L, w.max_seq_len, w.page_size, w.layer_kind,
-                                       args.split_keys), dtype=torch.uint8, device=dev)
+                                       args.work_groups), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
     log(f"inputs resident in HBM ({time.perf_counter() - t0:.1f} s)")
 
@@ -168,7 +170,7 @@ def main():
         P.attn_step(d["qkv"], d["positions"], d["table"], d["seq_lens"], kp, vp, w.kv_scale,
                     w.page_size, w.layer_kind, out, q_norm_w=d["w_q"], k_norm_w=d["w_k"],
                     o_norm_w=d["w_o"], max_seq_len=w.max_seq_len, workspace=ws,
-                    split_keys=args.split_keys, attn_events=events)
+                    work_groups=args.work_groups, attn_events=events)
 
     for _ in range(args.warmup):
         step()
@@ -229,7 +231,7 @@ def main():
     traffic = read_traffic(kv)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": traffic, "kernel": "attn_splitk_kernel (split-K attention)",
+                "traffic": traffic, "kernel": "attn_kernel (split-K attention + merge + gated norm)",
                 "algorithmic_bytes_per_launch": kv, "avg_launch_us": round(attn_avg_ms * 1e3, 2)}
 
     cpu = None
@@ -248,8 +250,8 @@ def main():
                    "ctx_min": int(w.ctx.min()), "ctx_max": int(w.ctx.max()),
                    "ctx_mean": round(float(w.ctx.mean()), 1), "keys": int(kv // 256),
                    "kv_bytes": kv, "pool_rows": w.num_rows, "seed": w.seed,
-                   "split_keys": P.split_keys(w.B, w.L, w.max_seq_len, w.layer_kind,
-                                              args.split_keys)},
+                   "work_groups": P.work_groups(w.B, w.L, w.max_seq_len, w.layer_kind,
+                                                args.work_groups)},
         "cold_cache_graph_replay": cold,
         "roofline": roofline,
         "cpu_baseline": cpu,

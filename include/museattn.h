@@ -75,14 +75,15 @@ enum museattn_status {
   MUSEATTN_ERR_NULL = -1,         /* a required pointer is null */
   MUSEATTN_ERR_PAGE_SIZE = -2,    /* page_size is not 1 or 64 */
   MUSEATTN_ERR_LAYER_KIND = -3,   /* layer_kind is not FULL or SLIDING */
-  MUSEATTN_ERR_SHAPE = -4,        /* B, L, max_seq_len or num_rows out of range */
+  MUSEATTN_ERR_SHAPE = -4,        /* B (1..1024), L (1..8), max_seq_len or
+                                     num_rows out of range */
   MUSEATTN_ERR_TABLE = -5,        /* table_stride < ceil(max_seq_len / page_size) */
   MUSEATTN_ERR_ALIGN = -6,        /* k_cache/v_cache not 16-byte aligned, or
                                      qkv/out/weights not naturally aligned */
   MUSEATTN_ERR_WORKSPACE = -7,    /* workspace smaller than museattn_workspace_bytes()
                                      or not 256-byte aligned */
   MUSEATTN_ERR_PARAM = -8,        /* kv_scale, eps, q_scale, rope_base or
-                                     split_keys out of range */
+                                     work_groups out of range */
   MUSEATTN_ERR_ALIAS = -9,        /* out overlaps qkv */
   MUSEATTN_ERR_LAUNCH = -10       /* a kernel launch failed */
 };
@@ -96,9 +97,10 @@ typedef struct museattn_params {
   float eps;               /* rmsnorm epsilon, >= 0 (1e-6) */
   float q_scale;           /* multiplier of the normed q (5.473) */
   float rope_base;         /* RoPE base, > 0 (10000) */
-  int split_keys;          /* keys per work-group along the key axis; 0 = chosen
-                              from the shapes, else a multiple of 32 in
-                              [32, 4096]. */
+  int work_groups;         /* attention work-groups, each taking an equal share
+                              of all requests' key chunks; 0 = chosen from the
+                              shapes, else 1..65535.  Changes only the
+                              summation order. */
 } museattn_params;
 
 /* Bytes of device workspace museattn_attn_step needs for these shapes (a
@@ -129,7 +131,7 @@ int museattn_check_args(const void *qkv, const int32_t *positions, const int32_t
  *   layer_kind MUSEATTN_FULL or MUSEATTN_SLIDING
  *   out        bf16 [B][L][1024]
  *   stream     hipStream_t the work is enqueued on (NULL = default stream)
- *   B >= 1, 1 <= L <= 8, table_stride >= ceil(max_seq_len / page_size),
+ *   1 <= B <= 1024, 1 <= L <= 8, table_stride >= ceil(max_seq_len / page_size),
  *   L <= max_seq_len <= 2^30, num_rows a multiple of page_size,
  *   workspace  device scratch of >= museattn_workspace_bytes(...) bytes,
  *              256-byte aligned. */
@@ -152,8 +154,9 @@ int museattn_attn_step_profiled(const void *qkv, const int32_t *positions, const
                                 size_t workspace_bytes, void *attn_start_event,
                                 void *attn_end_event);
 
-/* Keys per split the library uses for these shapes (split_keys = 0 chooses). */
-int museattn_split_keys(int B, int L, int max_seq_len, int layer_kind, const museattn_params *params);
+/* Attention work-groups the library launches for these shapes
+ * (params->work_groups = 0 chooses). */
+int museattn_work_groups(int B, int L, int max_seq_len, int layer_kind, const museattn_params *params);
 
 /* Static description of a status code. */
 const char *museattn_strerror(int status);

@@ -32,7 +32,7 @@ STATUS = {
 # every symbol include/museattn.h declares
 EXPORTS = ("museattn_abi_version", "museattn_strerror", "museattn_workspace_bytes",
            "museattn_check_args", "museattn_attn_step", "museattn_attn_step_profiled",
-           "museattn_split_keys")
+           "museattn_work_groups")
 
 
 class Params(ctypes.Structure):
@@ -43,7 +43,7 @@ class Params(ctypes.Structure):
         ("eps", ctypes.c_float),
         ("q_scale", ctypes.c_float),
         ("rope_base", ctypes.c_float),
-        ("split_keys", ctypes.c_int),
+        ("work_groups", ctypes.c_int),
     ]
 
 
@@ -72,8 +72,8 @@ def lib() -> ctypes.CDLL:
         L.museattn_strerror.argtypes = [i32]
         L.museattn_workspace_bytes.restype = ctypes.c_size_t
         L.museattn_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, pp]
-        L.museattn_split_keys.restype = i32
-        L.museattn_split_keys.argtypes = [i32, i32, i32, i32, pp]
+        L.museattn_work_groups.restype = i32
+        L.museattn_work_groups.argtypes = [i32, i32, i32, i32, pp]
         common = [vp, vp, vp, vp, vp, vp, f32, i32, i32, vp]
         L.museattn_check_args.restype = i32
         L.museattn_check_args.argtypes = common + [i32, i32, i32, i32, i64, pp, vp, ctypes.c_size_t]
@@ -95,15 +95,15 @@ def strerror(status: int) -> str:
 
 
 def make_params(q_norm_w=0, k_norm_w=0, o_norm_w=0, eps=DEFAULT_EPS, q_scale=DEFAULT_Q_SCALE,
-                rope_base=DEFAULT_ROPE_BASE, split_keys=0) -> Params:
+                rope_base=DEFAULT_ROPE_BASE, work_groups=0) -> Params:
     """Params from device pointers (ints) or tensors."""
     ptr = lambda x: x.data_ptr() if hasattr(x, "data_ptr") else int(x)  # noqa: E731
     return Params(ptr(q_norm_w), ptr(k_norm_w), ptr(o_norm_w), float(eps), float(q_scale),
-                  float(rope_base), int(split_keys))
+                  float(rope_base), int(work_groups))
 
 
-def workspace_bytes(B, L, max_seq_len, page_size, layer_kind, split_keys=0) -> int:
-    p = make_params(split_keys=split_keys)
+def workspace_bytes(B, L, max_seq_len, page_size, layer_kind, work_groups=0) -> int:
+    p = make_params(work_groups=work_groups)
     n = lib().museattn_workspace_bytes(int(B), int(L), int(max_seq_len), int(page_size),
                                        int(layer_kind), ctypes.byref(p))
     if n == 0:
@@ -111,10 +111,10 @@ def workspace_bytes(B, L, max_seq_len, page_size, layer_kind, split_keys=0) -> i
     return n
 
 
-def split_keys(B, L, max_seq_len, layer_kind, split_keys=0) -> int:
-    p = make_params(split_keys=split_keys)
-    return lib().museattn_split_keys(int(B), int(L), int(max_seq_len), int(layer_kind),
-                                     ctypes.byref(p))
+def work_groups(B, L, max_seq_len, layer_kind, work_groups=0) -> int:
+    p = make_params(work_groups=work_groups)
+    return lib().museattn_work_groups(int(B), int(L), int(max_seq_len), int(layer_kind),
+                                      ctypes.byref(p))
 
 
 def check_args(qkv, positions, table, seq_lens, k_cache, v_cache, kv_scale, page_size,
@@ -136,7 +136,7 @@ def _need(cond, msg):
 def attn_step(qkv, positions, table, seq_lens, k_cache, v_cache, kv_scale, page_size,
               layer_kind, out, stream=None, *, q_norm_w, k_norm_w, o_norm_w, max_seq_len,
               workspace=None, eps=DEFAULT_EPS, q_scale=DEFAULT_Q_SCALE,
-              rope_base=DEFAULT_ROPE_BASE, split_keys=0, attn_events=None):
+              rope_base=DEFAULT_ROPE_BASE, work_groups=0, attn_events=None):
     """One attention step on torch tensors (see include/museattn.h).
 
     qkv bf16 [B*L, 2304]; positions int32 [B*L]; table int32 [B, stride];
@@ -173,8 +173,8 @@ def attn_step(qkv, positions, table, seq_lens, k_cache, v_cache, kv_scale, page_
         _need(t.dtype == torch.uint8 and t.numel() % ROW_BYTES == 0, f"{name} must be uint8 rows of 128 B")
     _need(k_cache.numel() == v_cache.numel(), "k_cache and v_cache must hold the same rows")
     num_rows = k_cache.numel() // ROW_BYTES
-    params = make_params(q_norm_w, k_norm_w, o_norm_w, eps, q_scale, rope_base, split_keys)
-    need = workspace_bytes(B, L, max_seq_len, page_size, layer_kind, split_keys)
+    params = make_params(q_norm_w, k_norm_w, o_norm_w, eps, q_scale, rope_base, work_groups)
+    need = workspace_bytes(B, L, max_seq_len, page_size, layer_kind, work_groups)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     _need(workspace.is_cuda and workspace.dtype == torch.uint8, "workspace must be a uint8 device tensor")

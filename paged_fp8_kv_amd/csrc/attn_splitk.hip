@@ -1,9 +1,10 @@
 // Split-K attention over the paged FP8 cache: softmax(q . K^T / 8) . V for
 // every block token and query head (task page "Gated attention decode",
 // section "What to compute", line a = softmax(...); window and causal rules
-// from section "Shapes").  Each work-group owns one split of one request's
-// key axis and writes one partial (running max, sum, unnormalised output) per
-// (token, head); the combine kernel merges the splits.
+// from section "Shapes"), followed by the merge of the key-axis partials and
+// the gated output norm.  Work-groups take equal shares of all requests' key
+// chunks (see attn_kernel) and write one partial (reference max, sum,
+// unnormalised output) per (token, head) and segment; combine.hip merges them.
 //
 // Data path per 32-key chunk (one wave):
 //  * cache rows come from an LDS copy of the split's table entries, so the
@@ -23,9 +24,9 @@
 //    byte 8n+mt of the V row);
 //  * online softmax in base 2 (log2(e)/8 and kv_scale are folded into q).
 //
-// Decode (L = 1): the 4 waves take interleaved chunks of the split and merge
+// Decode (L = 1): the 4 waves take interleaved chunks of a segment and merge
 // their states in LDS.  Verify (L > 1): wave w owns tokens w and w+4 and
-// walks every chunk of the split (the re-reads of a row by the 4 waves hit
+// walks every chunk of the segment (the re-reads of a row by the 4 waves hit
 // the cache).
 #include "device_common.h"
 #include "launch.h"
@@ -34,6 +35,7 @@ namespace museattn {
 
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr int MAX_SPLIT_LDS = 4096;   // table entries cached per work-group
+constexpr float RESCALE_SLACK = 8.0f;  // log2 units a stale reference max may lag
 
 struct RowBuf {
   uint4 k[4];   // [tile*2 + kv head] 16 B of K row
@@ -150,30 +152,43 @@ __device__ __forceinline__ void compute_chunk(const RowBuf &rb, int u0, int j,
       s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[1][kk], q[tk].lo[kk], s1, 0, 0, 0);
     }
     float sc[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
-    float cmax = -INFINITY;
+    // only a chunk that straddles the token's visible range needs a mask
+    if (u0 < st.lo || u0 + CHUNK - 1 > st.hi) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int u = u0 + (i >> 2) * 16 + 4 * j + (i & 3);
-      if (u < st.lo || u > st.hi) sc[i] = -INFINITY;
-      cmax = fmaxf(cmax, sc[i]);
+      for (int i = 0; i < 8; ++i) {
+        const int u = u0 + (i >> 2) * 16 + 4 * j + (i & 3);
+        if (u < st.lo || u > st.hi) sc[i] = -INFINITY;
+      }
     }
+    float cmax = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
+                       fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
     cmax = head_max(cmax);
-    const float mnew = fmaxf(st.m, cmax);
-    const float muse = mnew == -INFINITY ? 0.0f : mnew;
-    const float alpha = __builtin_amdgcn_exp2f(st.m - muse);
-    if (__any(alpha != 1.0f)) {
+    // Lazy rescale: the reference max st.m only moves when some head's chunk
+    // max exceeds it by more than RESCALE_SLACK (log2 units), so P <= 2^SLACK.
+    // Any reference gives the same softmax; this one skips most rescales.
+    if (__any(cmax > st.m + RESCALE_SLACK)) {
+      const float mnew = fmaxf(st.m, cmax);
+      const float alpha = mnew == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(st.m - mnew);
       st.l *= alpha;
 #pragma unroll
       for (int mt = 0; mt < 8; ++mt) st.o[mt] *= alpha;
+      st.m = mnew;
     }
-    st.m = mnew;
-    bf16x8 ph, pl;
+    const float muse = st.m == -INFINITY ? 0.0f : st.m;
+    float pv[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const float pv = __builtin_amdgcn_exp2f(sc[i] - muse);
-      st.l += pv;
-      ph[i] = (__bf16)pv;
-      pl[i] = (__bf16)(pv - (float)ph[i]);
+      pv[i] = __builtin_amdgcn_exp2f(sc[i] - muse);
+      st.l += pv[i];
+    }
+    bf16x8 ph, pl;
+#pragma unroll
+    for (int i = 0; i < 8; i += 2) {
+      const f32x2 f = {pv[i], pv[i + 1]};
+      const bf16x2 h = __builtin_convertvector(f, bf16x2);
+      const bf16x2 r = __builtin_convertvector(f - __builtin_convertvector(h, f32x2), bf16x2);
+      ph[i] = h[0]; ph[i + 1] = h[1];
+      pl[i] = r[0]; pl[i + 1] = r[1];
     }
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt) {
@@ -185,16 +200,20 @@ __device__ __forceinline__ void compute_chunk(const RowBuf &rb, int u0, int j,
 
 // B operand of S^T = K . Q^T for token t: lane (n, j), K-step kk holds
 // q[t][n][16j + 8(kk%2) + i] (i < 8) when head n belongs to KV head kk/2, else 0.
+// The loads are unconditional (always in bounds) so they issue as one batch.
 __device__ __forceinline__ void load_q(const StepArgs &a, int t, int n, int j, float qmul,
                                        QOps &qo) {
-  const float *qrow = a.qbuf + ((size_t)t * HQ + n) * D;
+  const float *qrow = a.qbuf + ((size_t)t * HQ + n) * D + 16 * j;
+  const f32x4 *q4 = reinterpret_cast<const f32x4 *>(qrow);
+  f32x4 v[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v[i] = q4[i];
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
-    const bool mine = (n >> 3) == (kk >> 1);
-    const int d0 = 16 * j + 8 * (kk & 1);
+    const float mul = (n >> 3) == (kk >> 1) ? qmul : 0.0f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const float x = mine ? qrow[d0 + i] * qmul : 0.0f;
+      const float x = v[2 * (kk & 1) + (i >> 2)][i & 3] * mul;
       const __bf16 h = (__bf16)x;
       qo.hi[kk][i] = h;
       qo.lo[kk][i] = (__bf16)(x - (float)h);
@@ -202,31 +221,34 @@ __device__ __forceinline__ void load_q(const StepArgs &a, int t, int n, int j, f
   }
 }
 
-template <int MODE, int NT, int NBUF>
-__global__ __launch_bounds__(256) void attn_splitk_kernel(StepArgs a) {
-  __shared__ __attribute__((aligned(16))) uint32_t lrows[MAX_SPLIT_LDS];
-  __shared__ float sm_m[WAVES][HQ];
-  __shared__ float sm_l[WAVES][HQ];
-  __shared__ __attribute__((aligned(16))) float sm_o[MODE == 0 ? WAVES : 1][HQ][D];
+// Row buffers in flight per wave (decode) and the waves-per-SIMD target the
+// register allocation aims for.
+#ifndef MUSEATTN_DECODE_NBUF
+#define MUSEATTN_DECODE_NBUF 2
+#endif
+#ifndef MUSEATTN_DECODE_MIN_WAVES
+#define MUSEATTN_DECODE_MIN_WAVES 2
+#endif
 
-  const int s = blockIdx.x, b = blockIdx.y;
+constexpr int PIECE_CHUNKS = MAX_SPLIT_LDS / CHUNK;   // chunks whose rows one LDS fill holds
+
+struct Lds {
+  uint32_t lrows[MAX_SPLIT_LDS];
+  float sm_o[WAVES][HQ][D];
+  float sm_m[WAVES][HQ];
+  float sm_l[WAVES][HQ];
+  int pref[MAX_BATCH + 1];
+  int scan[256];
+};
+
+// One segment: chunks [x, y) of request b's key range (chunk i = keys
+// kbase + 32i ..), processed by the whole work-group, leaving one partial per
+// (token, head) in slot `slot`.
+template <int MODE, int NT, int NBUF>
+__device__ __forceinline__ void process_segment(const StepArgs &a, int b, const KeyRange &r, int x,
+                                                int y, int slot, Lds &sh) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int n = lane & 15, j = lane >> 4;
-
-  const KeyRange r = request_range(a, b);
-  if (s >= valid_splits(a, r)) return;   // uniform over the work-group
-  const int kstart = r.kbase + s * a.split_keys;
-  int kend = kstart + a.split_keys;
-  kend = kend < r.khi + 1 ? kend : r.khi + 1;
-  const int nchunks = (kend - kstart + CHUNK - 1) / CHUNK;
-
-  // cache rows of the split's keys (clamped into [klo, khi])
-  for (int i = tid; i < nchunks * CHUNK; i += 256) {
-    int u = kstart + i;
-    u = u < r.klo ? r.klo : (u > r.khi ? r.khi : u);
-    lrows[i] = cache_row(a, b, u);
-  }
-
   const float qmul = a.kv_scale * (LOG2E / 8.0f);
   TokState ts[NT];
   QOps qo[NT];
@@ -244,31 +266,61 @@ __global__ __launch_bounds__(256) void attn_splitk_kernel(StepArgs a) {
     for (int mt = 0; mt < 8; ++mt) ts[tk].o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
     load_q(a, t, n, j, qmul, qo[tk]);
   }
-  __syncthreads();
-
-  const int c0 = MODE == 0 ? wave : 0;
-  const int cstep = MODE == 0 ? WAVES : 1;
   bool any_live = false;
 #pragma unroll
   for (int tk = 0; tk < NT; ++tk) any_live |= ts[tk].live;
 
-  if (any_live) {
-    RowBuf buf[NBUF];
+  const int nseg = y - x;
+  const int npieces = (nseg + PIECE_CHUNKS - 1) / PIECE_CHUNKS;
+  for (int pc = 0; pc < npieces; ++pc) {
+    const int px = x + (int)((int64_t)pc * nseg / npieces);
+    const int py = x + (int)((int64_t)(pc + 1) * nseg / npieces);
+    const int nchunks = py - px;
+    const int kstart = r.kbase + px * CHUNK;
+    __syncthreads();   // every wave is done with the previous rows
+    {
+      // cache rows of the piece's keys (clamped into [klo, khi]) as one batch
+      uint32_t rows[MAX_SPLIT_LDS / 256];
 #pragma unroll
-    for (int k = 0; k < NBUF; ++k) {
-      const int c = c0 + k * cstep;
-      if (c < nchunks) load_rows(buf[k], a.k_cache, a.v_cache, lrows + c * CHUNK, n, j);
+      for (int it = 0; it < MAX_SPLIT_LDS / 256; ++it) {
+        int u = kstart + tid + it * 256;
+        u = u < r.klo ? r.klo : (u > r.khi ? r.khi : u);
+        rows[it] = cache_row(a, b, u);
+      }
+#pragma unroll
+      for (int it = 0; it < MAX_SPLIT_LDS / 256; ++it) sh.lrows[tid + it * 256] = rows[it];
     }
-    for (int c = c0; c < nchunks; c += NBUF * cstep) {
+    __syncthreads();
+
+    // This wave's chunks of the piece: c0, c0 + cstep, ... (nloc of them).  In
+    // the steady state every load is unconditional -- chunk indices past the
+    // end are clamped to the last chunk -- so the compiler can count the loads
+    // in flight and wait only for the buffer it is about to use.
+    const int c0 = MODE == 0 ? wave : 0;
+    const int cstep = MODE == 0 ? WAVES : 1;
+    const int nloc = nchunks > c0 ? (nchunks - c0 + cstep - 1) / cstep : 0;
+    if (any_live && nloc > 0) {
+      const int last = nloc - 1;
+      RowBuf buf[NBUF];
 #pragma unroll
       for (int k = 0; k < NBUF; ++k) {
-        const int cc = c + k * cstep;
-        if (cc < nchunks) {
-          compute_chunk<NT>(buf[k], kstart + cc * CHUNK, j, ts, qo);
-          const int cn = cc + NBUF * cstep;
-          if (cn < nchunks) load_rows(buf[k], a.k_cache, a.v_cache, lrows + cn * CHUNK, n, j);
+        const int i = k < last ? k : last;
+        load_rows(buf[k], a.k_cache, a.v_cache, sh.lrows + (c0 + i * cstep) * CHUNK, n, j);
+      }
+      int i = 0;
+      for (; i + NBUF <= nloc; i += NBUF) {
+#pragma unroll
+        for (int k = 0; k < NBUF; ++k) {
+          compute_chunk<NT>(buf[k], kstart + (c0 + (i + k) * cstep) * CHUNK, j, ts, qo);
+          int inext = i + k + NBUF;
+          inext = inext < last ? inext : last;
+          load_rows(buf[k], a.k_cache, a.v_cache, sh.lrows + (c0 + inext * cstep) * CHUNK, n, j);
         }
       }
+#pragma unroll
+      for (int k = 0; k < NBUF - 1; ++k)
+        if (i + k < nloc)
+          compute_chunk<NT>(buf[k], kstart + (c0 + (i + k) * cstep) * CHUNK, j, ts, qo);
     }
   }
 
@@ -280,13 +332,13 @@ __global__ __launch_bounds__(256) void attn_splitk_kernel(StepArgs a) {
   if (MODE == 0) {
     const float lsum = head_sum(ts[0].l);
     if (j == 0) {
-      sm_m[wave][n] = ts[0].m;
-      sm_l[wave][n] = lsum;
+      sh.sm_m[wave][n] = ts[0].m;
+      sh.sm_l[wave][n] = lsum;
     }
     if (own) {
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
-        float *dst = &sm_o[wave][n][dbase + 8 * rr];
+        float *dst = &sh.sm_o[wave][n][dbase + 8 * rr];
         *reinterpret_cast<f32x4 *>(dst) =
             f32x4{ts[0].o[0][rr], ts[0].o[1][rr], ts[0].o[2][rr], ts[0].o[3][rr]};
         *reinterpret_cast<f32x4 *>(dst + 4) =
@@ -298,38 +350,38 @@ __global__ __launch_bounds__(256) void attn_splitk_kernel(StepArgs a) {
     const int h = tid >> 4, d4 = (tid & 15) * 4;
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < WAVES; ++w) M = fmaxf(M, sm_m[w][h]);
+    for (int w = 0; w < WAVES; ++w) M = fmaxf(M, sh.sm_m[w][h]);
     f32x4 o = {0.f, 0.f, 0.f, 0.f};
     float lt = 0.0f;
     if (M != -INFINITY) {
 #pragma unroll
       for (int w = 0; w < WAVES; ++w) {
-        const float sc = __builtin_amdgcn_exp2f(sm_m[w][h] - M);
-        lt += sc * sm_l[w][h];
-        o += sc * *reinterpret_cast<const f32x4 *>(&sm_o[w][h][d4]);
+        const float sc = __builtin_amdgcn_exp2f(sh.sm_m[w][h] - M);
+        lt += sc * sh.sm_l[w][h];
+        o += sc * *reinterpret_cast<const f32x4 *>(&sh.sm_o[w][h][d4]);
       }
     }
-    const size_t slot = ((size_t)b * HQ + h) * a.nsplit + s;   // token t = b (L = 1)
-    *reinterpret_cast<f32x4 *>(a.part_o + slot * D + d4) = o;
+    const size_t e = (size_t)slot * HQ + h;   // L = 1
+    *reinterpret_cast<f32x4 *>(a.part_o + e * D + d4) = o;
     if ((tid & 15) == 0) {
-      a.part_ml[slot * 2] = M;
-      a.part_ml[slot * 2 + 1] = lt;
+      a.part_ml[e * 2] = M;
+      a.part_ml[e * 2 + 1] = lt;
     }
   } else {
 #pragma unroll
     for (int tk = 0; tk < NT; ++tk) {
       const float lsum = head_sum(ts[tk].l);
       if (!ts[tk].live) continue;
-      const int t = b * a.L + wave + WAVES * tk;
-      const size_t slot = ((size_t)t * HQ + n) * a.nsplit + s;
+      const int jt = wave + WAVES * tk;
+      const size_t e = ((size_t)slot * a.L + jt) * HQ + n;
       if (j == 0) {
-        a.part_ml[slot * 2] = ts[tk].m;
-        a.part_ml[slot * 2 + 1] = lsum;
+        a.part_ml[e * 2] = ts[tk].m;
+        a.part_ml[e * 2 + 1] = lsum;
       }
       if (own) {
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
-          float *dst = a.part_o + slot * D + dbase + 8 * rr;
+          float *dst = a.part_o + e * D + dbase + 8 * rr;
           *reinterpret_cast<f32x4 *>(dst) =
               f32x4{ts[tk].o[0][rr], ts[tk].o[1][rr], ts[tk].o[2][rr], ts[tk].o[3][rr]};
           *reinterpret_cast<f32x4 *>(dst + 4) =
@@ -340,14 +392,83 @@ __global__ __launch_bounds__(256) void attn_splitk_kernel(StepArgs a) {
   }
 }
 
+// The attention kernel.  Every work-group derives the same plan from the
+// device-side sequence lengths: request b spans chunks [pref[b], pref[b+1]) of
+// the concatenated chunk space, and work-group w takes an equal contiguous
+// share of it, so no work-group idles while another still has a long split.
+// A share that crosses request boundaries is processed one segment per
+// request; segment (w, b) writes its partial to slot w + b (slots are unique
+// because both w and b grow along the chunk space).  The combine kernel then
+// merges each request's slots.
+template <int MODE, int NT, int NBUF>
+__global__ __launch_bounds__(256, MODE == 0 ? MUSEATTN_DECODE_MIN_WAVES : 1) void attn_kernel(StepArgs a) {
+  __shared__ __attribute__((aligned(16))) Lds sh;
+  const int tid = threadIdx.x;
+
+  // chunk-count prefix sums over the requests (4 per thread, B <= 1024)
+  int cnt[4], sum = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int b = 4 * tid + k;
+    cnt[k] = b < a.B ? request_chunks(request_range(a, b)) : 0;
+    sum += cnt[k];
+  }
+  sh.scan[tid] = sum;
+  __syncthreads();
+  for (int off = 1; off < 256; off <<= 1) {
+    const int v = tid >= off ? sh.scan[tid - off] : 0;
+    __syncthreads();
+    sh.scan[tid] += v;
+    __syncthreads();
+  }
+  {
+    int run = sh.scan[tid] - sum;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int b = 4 * tid + k;
+      if (b < a.B) sh.pref[b] = run;
+      run += cnt[k];
+    }
+    if (tid == 255) sh.pref[a.B] = sh.scan[255];
+  }
+  __syncthreads();
+  const int64_t C = sh.pref[a.B];
+  const int w = blockIdx.x;
+
+  const int G = C < a.work_groups ? (int)C : a.work_groups;
+  if (w == 0) {
+    // the plan, for the combine kernel: chunk prefix sums and work-groups used
+    for (int i = tid; i <= a.B; i += 256) a.plan[i] = sh.pref[i];
+    if (tid == 0) a.plan[a.B + 1] = G;
+  }
+  if (w >= G) return;   // uniform over the work-group
+  const int64_t cb = (int64_t)w * C / G, ce = (int64_t)(w + 1) * C / G;
+  int b = 0;
+  {
+    int hi = a.B - 1;
+    while (b < hi) {   // largest b with pref[b] <= cb
+      const int mid = (b + hi + 1) >> 1;
+      if (sh.pref[mid] <= cb) b = mid; else hi = mid - 1;
+    }
+  }
+  for (; b < a.B && sh.pref[b] < ce; ++b) {
+    const int64_t p0 = sh.pref[b], p1 = sh.pref[b + 1];
+    const int x = (int)((cb > p0 ? cb : p0) - p0);
+    const int y = (int)((ce < p1 ? ce : p1) - p0);
+    if (y <= x) continue;
+    const KeyRange r = request_range(a, b);
+    process_segment<MODE, NT, NBUF>(a, b, r, x, y, w + b, sh);
+  }
+}
+
 void launch_attn(const StepArgs &a, hipStream_t stream) {
-  const dim3 grid(a.nsplit, a.B), block(256);
+  const dim3 grid(a.work_groups), block(256);
   if (a.L == 1)
-    hipLaunchKernelGGL((attn_splitk_kernel<0, 1, 3>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((attn_kernel<0, 1, MUSEATTN_DECODE_NBUF>), grid, block, 0, stream, a);
   else if (a.L <= WAVES)
-    hipLaunchKernelGGL((attn_splitk_kernel<1, 1, 2>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((attn_kernel<1, 1, 2>), grid, block, 0, stream, a);
   else
-    hipLaunchKernelGGL((attn_splitk_kernel<1, 2, 2>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((attn_kernel<1, 2, 2>), grid, block, 0, stream, a);
 }
 
 }  // namespace museattn

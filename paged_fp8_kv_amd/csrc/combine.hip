@@ -1,49 +1,80 @@
-// Merge of the split partials and the gated output norm: a = (sum_s o_s 2^(m_s-M))
-// / (sum_s l_s 2^(m_s-M)) * kv_scale, then out = rmsnorm(a) * w_o * sigmoid(gate)
-// per head in bf16 (task page "Gated attention decode", section "What to
-// compute", last line of the listing; output shape from the same section).
+// Merge of the key-axis partials and the gated output norm: for token t and
+// head h, a = sum_s o_s 2^(m_s - M) / sum_s l_s 2^(m_s - M) * kv_scale over the
+// slots of t's request, then out = rmsnorm(a) * w_o * sigmoid(gate) in bf16
+// (task page "Gated attention decode", section "What to compute", last line
+// of the listing; output shape from the same section).
 //
-// One wave per (token, head); lane d owns output dim d.
+// One 256-thread work-group per (token, head): 16 slot lanes x 16 dimension
+// quads accumulate the rescaled partials with independent loads, LDS sums the
+// slot lanes, and one wave finishes the gated norm.
 #include "device_common.h"
 #include "launch.h"
 
 namespace museattn {
 
-__global__ __launch_bounds__(64) void combine_kernel(StepArgs a) {
+__global__ __launch_bounds__(256) void combine_kernel(StepArgs a) {
+  __shared__ float sm_max[4];
+  __shared__ __attribute__((aligned(16))) float sm_o[16][D];
+  __shared__ float sm_l[16];
+
   const int th = blockIdx.x;          // t * 16 + h
   const int t = th / HQ, h = th % HQ;
-  const int d = threadIdx.x;
-  const int b = t / a.L;
-  const KeyRange r = request_range(a, b);
-  const int ns = valid_splits(a, r);
-  const float *ml = a.part_ml + (size_t)th * a.nsplit * 2;
-  const float *po = a.part_o + (size_t)th * a.nsplit * D;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int b = t / a.L, jt = t % a.L;
+  const int64_t p0 = a.plan[b], p1 = a.plan[b + 1], C = a.plan[a.B];
+  const int G = a.plan[a.B + 1];
+  // slots of request b: w + b for the work-groups w whose share meets its chunks
+  int s0 = 0, s1 = -1;
+  if (p1 > p0) {
+    s0 = wg_of_chunk(p0, C, G) + b;
+    s1 = wg_of_chunk(p1 - 1, C, G) + b;
+  }
+  const float2 *ml = reinterpret_cast<const float2 *>(a.part_ml);
+  const f32x4 *po = reinterpret_cast<const f32x4 *>(a.part_o);
+  auto entry = [&](int s) { return ((size_t)s * a.L + jt) * HQ + h; };
 
-  float M = -INFINITY;
-  for (int s = d; s < ns; s += 64) M = fmaxf(M, ml[2 * s]);
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
+  float m = -INFINITY;
+  for (int s = s0 + tid; s <= s1; s += 256) m = fmaxf(m, ml[entry(s)].x);
+  m = wave_max(m);
+  if (lane == 0) sm_max[wave] = m;
+  __syncthreads();
+  const float M = fmaxf(fmaxf(sm_max[0], sm_max[1]), fmaxf(sm_max[2], sm_max[3]));
 
-  float lsum = 0.0f, o = 0.0f;
+  const int sl = tid >> 4, dq = tid & 15;
+  f32x4 o = {0.f, 0.f, 0.f, 0.f};
+  float l = 0.0f;
   if (M != -INFINITY) {
-#pragma unroll 8
-    for (int s = 0; s < ns; ++s) {
-      const float ms = ml[2 * s];
-      const float sc = ms == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(ms - M);
-      lsum += sc * ml[2 * s + 1];
-      o += sc * po[(size_t)s * D + d];
+#pragma unroll 4
+    for (int s = s0 + sl; s <= s1; s += 16) {
+      const size_t e = entry(s);
+      const float2 v = ml[e];
+      const float sc = v.x == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(v.x - M);
+      l += sc * v.y;
+      o += sc * po[e * (D / 4) + dq];
     }
   }
-  const float av = lsum > 0.0f ? o / lsum * a.kv_scale : 0.0f;
-  const float ms2 = wave_sum(av * av) * (1.0f / 64.0f);
-  const float y = av / sqrtf(ms2 + a.eps) * a.wo[d];
-  const float g = bf16_bits_to_f32(a.qkv[(size_t)t * QKV_W + G_OFF + h * D + d]);
-  const float gated = y / (1.0f + expf(-g));
-  a.out[(size_t)t * (HQ * D) + h * D + d] = f32_to_bf16_bits(gated);
+  *reinterpret_cast<f32x4 *>(&sm_o[sl][4 * dq]) = o;
+  if (dq == 0) sm_l[sl] = l;
+  __syncthreads();
+
+  if (wave == 0) {
+    const int d = lane;
+    float od = 0.0f, lsum = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      od += sm_o[k][d];
+      lsum += sm_l[k];
+    }
+    const float av = lsum > 0.0f ? od / lsum * a.kv_scale : 0.0f;
+    const float ms2 = wave_sum(av * av) * (1.0f / 64.0f);
+    const float y = av / sqrtf(ms2 + a.eps) * a.wo[d];
+    const float g = bf16_bits_to_f32(a.qkv[(size_t)t * QKV_W + G_OFF + h * D + d]);
+    a.out[(size_t)t * (HQ * D) + h * D + d] = f32_to_bf16_bits(y / (1.0f + expf(-g)));
+  }
 }
 
 void launch_combine(const StepArgs &a, hipStream_t stream) {
-  hipLaunchKernelGGL(combine_kernel, dim3(a.B * a.L * HQ), dim3(64), 0, stream, a);
+  hipLaunchKernelGGL(combine_kernel, dim3(a.B * a.L * HQ), dim3(256), 0, stream, a);
 }
 
 }  // namespace museattn

@@ -16,10 +16,12 @@ constexpr int ROW = 128;     // bytes of one cache row (2 KV heads x 64 E4M3 byt
 constexpr int WINDOW = 2048; // sliding window, the query's own position included
 constexpr int CHUNK = 32;    // keys per step of the attention kernel's inner loop
 constexpr int WAVES = 4;     // waves per attention work-group
+constexpr int MAX_BATCH = 1024;   // requests per call (prefix sums live in LDS)
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 // Everything one step's kernels read, passed by value.
 struct StepArgs {
@@ -32,12 +34,15 @@ struct StepArgs {
   uint16_t *out;           // bf16 bits [T][1024]
   const float *wq, *wk, *wo;
   float *qbuf;             // [T][16][64] normed, rotated, scaled q
-  float *part_ml;          // [T][16][nsplit][2]  (running max in log2 units, sum)
-  float *part_o;           // [T][16][nsplit][64] unnormalised partial outputs
+  int *plan;               // [B + 2]: chunk prefix sums of the requests, then the
+                           // work-groups used (written by attention work-group 0)
+  float *part_ml;          // [slot][L][16][2] (reference max in log2 units, sum)
+  float *part_o;           // [slot][L][16][64] unnormalised partial outputs
   int64_t num_rows;
   float kv_scale, eps, q_scale, rope_base;
   int B, L, table_stride, max_seq_len, page_size, sliding;
-  int nsplit, split_keys;
+  int work_groups;         // attention work-groups launched (each takes an equal
+                           // share of all requests' key chunks)
 };
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t h) {
@@ -84,17 +89,57 @@ __device__ __forceinline__ KeyRange request_range(const StepArgs &a, int b) {
   return r;
 }
 
-// Splits of the key axis that hold keys of request b (the others are idle).
-__device__ __forceinline__ int valid_splits(const StepArgs &a, const KeyRange &r) {
-  if (r.khi < r.klo) return 0;
-  int n = (r.khi + 1 - r.kbase + a.split_keys - 1) / a.split_keys;
-  return n < a.nsplit ? n : a.nsplit;
+// Chunks (of CHUNK keys, from kbase) that request b's key range spans.
+__device__ __forceinline__ int request_chunks(const KeyRange &r) {
+  return r.khi < r.klo ? 0 : (r.khi + 1 - r.kbase + CHUNK - 1) / CHUNK;
 }
 
+// Sum over the 64 lanes of a wave, result in every lane: DPP steps inside each
+// 16-lane row (xor 1, xor 2, half-row mirror, row mirror), then the gfx950
+// row swaps across rows.  VALU only, no LDS round trip.
+#define MUSEATTN_DPP(x, ctrl) \
+  __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), (ctrl), 0xf, 0xf, false))
+
 __device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
+  x += MUSEATTN_DPP(x, 0xB1);    // quad_perm [1,0,3,2]
+  x += MUSEATTN_DPP(x, 0x4E);    // quad_perm [2,3,0,1]
+  x += MUSEATTN_DPP(x, 0x141);   // row_half_mirror
+  x += MUSEATTN_DPP(x, 0x140);   // row_mirror
+  int xi = __float_as_int(x);
+  auto p = __builtin_amdgcn_permlane16_swap(xi, xi, false, false);
+  x = __int_as_float(p[0]) + __int_as_float(p[1]);
+  xi = __float_as_int(x);
+  auto q = __builtin_amdgcn_permlane32_swap(xi, xi, false, false);
+  return __int_as_float(q[0]) + __int_as_float(q[1]);
+}
+
+// Chunk c of C chunks spread over G work-groups (work-group w owns chunks
+// [floor(w C / G), floor((w + 1) C / G))) belongs to work-group
+// floor(((c + 1) G - 1) / C).
+__device__ __forceinline__ int wg_of_chunk(int64_t c, int64_t C, int G) {
+  return (int)(((c + 1) * G - 1) / C);
+}
+
+// Sum over each 16-lane row (DPP only).
+__device__ __forceinline__ float row16_sum(float x) {
+  x += MUSEATTN_DPP(x, 0xB1);
+  x += MUSEATTN_DPP(x, 0x4E);
+  x += MUSEATTN_DPP(x, 0x141);
+  x += MUSEATTN_DPP(x, 0x140);
   return x;
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+  x = fmaxf(x, MUSEATTN_DPP(x, 0xB1));
+  x = fmaxf(x, MUSEATTN_DPP(x, 0x4E));
+  x = fmaxf(x, MUSEATTN_DPP(x, 0x141));
+  x = fmaxf(x, MUSEATTN_DPP(x, 0x140));
+  int xi = __float_as_int(x);
+  auto p = __builtin_amdgcn_permlane16_swap(xi, xi, false, false);
+  x = fmaxf(__int_as_float(p[0]), __int_as_float(p[1]));
+  xi = __float_as_int(x);
+  auto q = __builtin_amdgcn_permlane32_swap(xi, xi, false, false);
+  return fmaxf(__int_as_float(q[0]), __int_as_float(q[1]));
 }
 
 }  // namespace museattn

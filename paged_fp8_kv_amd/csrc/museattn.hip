@@ -1,4 +1,4 @@
-// Host side of libmuseattn: argument validation, the split schedule (a function
+// Host side of libmuseattn: argument validation, the launch shape (a function
 // of host shapes only, so a call can be captured into a HIP graph), workspace
 // layout and the three launches.  See include/museattn.h for the contract.
 #include <cmath>
@@ -11,59 +11,36 @@
 namespace museattn {
 namespace {
 
-constexpr int MAX_SPLIT = 4096;     // table entries one work-group caches in LDS
-constexpr int MAX_B = 65535;        // grid.y limit
+constexpr int MAX_WORK_GROUPS = 65535;
 constexpr int MAX_SEQ = 1 << 30;
 
 bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
-// Upper bound of one request's key span (from the first block token's window
-// start, rounded down to a chunk, to the last key).
-int64_t span_max(int L, int max_seq_len, int layer_kind) {
-  if (layer_kind == MUSEATTN_SLIDING) {
-    const int64_t s = (int64_t)L + WINDOW - 1 + (CHUNK - 1);
-    return s < max_seq_len ? s : max_seq_len;
-  }
-  return max_seq_len;
-}
-
-int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
-
-// Keys per work-group.  Decode aims at ~2048 work-groups (8 per CU) so the
-// last wave of work-groups is short; verify blocks do 8x the work per key, so
-// they aim at ~256 larger splits to keep the partials small.
-int choose_split(int B, int L, int max_seq_len, int layer_kind, int requested) {
+// Attention work-groups.  Each takes an equal share of all requests' key
+// chunks, so two per CU (the kernel's occupancy on MI355X's 256 CUs) keep
+// every CU busy to the end without a tail.  Verify blocks write 8x larger
+// partials, so they use one per CU.
+int choose_work_groups(int L, int requested) {
   if (requested > 0) return requested;
-  const int64_t work = (int64_t)B * span_max(L, max_seq_len, layer_kind);
-  int64_t s;
-  if (L == 1) {
-    s = round_up((work + 2047) / 2048, 128);
-    s = s < 128 ? 128 : s;
-  } else {
-    s = round_up((work + 255) / 256, CHUNK);
-    s = s < 64 ? 64 : s;
-  }
-  return (int)(s > MAX_SPLIT ? MAX_SPLIT : s);
+  return L == 1 ? 512 : 256;
 }
-
-bool split_ok(int split) { return split >= CHUNK && split <= MAX_SPLIT && split % CHUNK == 0; }
 
 struct Layout {
-  int split, nsplit;
-  size_t q_off, ml_off, o_off, total;
+  int work_groups;
+  size_t q_off, plan_off, ml_off, o_off, total;
 };
 
-Layout layout(int B, int L, int max_seq_len, int layer_kind, int split) {
+Layout layout(int B, int L, int work_groups) {
   Layout ly;
-  ly.split = split;
-  const int64_t span = span_max(L, max_seq_len, layer_kind);
-  ly.nsplit = (int)((span + split - 1) / split);
+  ly.work_groups = work_groups;
   const size_t T = (size_t)B * L;
+  const size_t slots = (size_t)work_groups + B;   // partial slots w + b
   auto al = [](size_t x) { return (x + 255) / 256 * 256; };
   ly.q_off = 0;
-  ly.ml_off = al(T * HQ * D * sizeof(float));
-  ly.o_off = ly.ml_off + al(T * HQ * (size_t)ly.nsplit * 2 * sizeof(float));
-  ly.total = ly.o_off + al(T * HQ * (size_t)ly.nsplit * D * sizeof(float));
+  ly.plan_off = al(T * HQ * D * sizeof(float));
+  ly.ml_off = ly.plan_off + al(((size_t)B + 2) * sizeof(int));
+  ly.o_off = ly.ml_off + al(slots * L * HQ * 2 * sizeof(float));
+  ly.total = ly.o_off + al(slots * L * HQ * D * sizeof(float));
   return ly;
 }
 
@@ -71,10 +48,10 @@ int check_shapes(int B, int L, int max_seq_len, int page_size, int layer_kind,
                  const museattn_params *params) {
   if (page_size != 1 && page_size != 64) return MUSEATTN_ERR_PAGE_SIZE;
   if (layer_kind != MUSEATTN_FULL && layer_kind != MUSEATTN_SLIDING) return MUSEATTN_ERR_LAYER_KIND;
-  if (B < 1 || B > MAX_B || L < 1 || L > 8 || max_seq_len < L || max_seq_len > MAX_SEQ)
+  if (B < 1 || B > MAX_BATCH || L < 1 || L > 8 || max_seq_len < L || max_seq_len > MAX_SEQ)
     return MUSEATTN_ERR_SHAPE;
   if (params == nullptr) return MUSEATTN_ERR_NULL;
-  if (params->split_keys != 0 && !split_ok(params->split_keys)) return MUSEATTN_ERR_PARAM;
+  if (params->work_groups < 0 || params->work_groups > MAX_WORK_GROUPS) return MUSEATTN_ERR_PARAM;
   return MUSEATTN_OK;
 }
 
@@ -97,23 +74,22 @@ const char *museattn_strerror(int status) {
     case MUSEATTN_ERR_TABLE: return "table_stride < ceil(max_seq_len / page_size)";
     case MUSEATTN_ERR_ALIGN: return "misaligned pointer (caches need 16-byte alignment)";
     case MUSEATTN_ERR_WORKSPACE: return "workspace too small or not 256-byte aligned";
-    case MUSEATTN_ERR_PARAM: return "kv_scale, eps, q_scale, rope_base or split_keys out of range";
+    case MUSEATTN_ERR_PARAM: return "kv_scale, eps, q_scale, rope_base or work_groups out of range";
     case MUSEATTN_ERR_ALIAS: return "out overlaps qkv";
     case MUSEATTN_ERR_LAUNCH: return "kernel launch failed";
     default: return "unknown status";
   }
 }
 
-int museattn_split_keys(int B, int L, int max_seq_len, int layer_kind, const museattn_params *params) {
+int museattn_work_groups(int B, int L, int max_seq_len, int layer_kind, const museattn_params *params) {
   if (check_shapes(B, L, max_seq_len, 1, layer_kind, params) != MUSEATTN_OK) return 0;
-  return choose_split(B, L, max_seq_len, layer_kind, params->split_keys);
+  return choose_work_groups(L, params->work_groups);
 }
 
 size_t museattn_workspace_bytes(int B, int L, int max_seq_len, int page_size, int layer_kind,
                                 const museattn_params *params) {
   if (check_shapes(B, L, max_seq_len, page_size, layer_kind, params) != MUSEATTN_OK) return 0;
-  const int split = choose_split(B, L, max_seq_len, layer_kind, params->split_keys);
-  return layout(B, L, max_seq_len, layer_kind, split).total;
+  return layout(B, L, choose_work_groups(L, params->work_groups)).total;
 }
 
 int museattn_check_args(const void *qkv, const int32_t *positions, const int32_t *table,
@@ -160,8 +136,7 @@ int museattn_attn_step_profiled(const void *qkv, const int32_t *positions, const
                                      page_size, layer_kind, out, B, L, table_stride, max_seq_len,
                                      num_rows, params, workspace, workspace_bytes);
   if (st != MUSEATTN_OK) return st;
-  const int split = choose_split(B, L, max_seq_len, layer_kind, params->split_keys);
-  const Layout ly = layout(B, L, max_seq_len, layer_kind, split);
+  const Layout ly = layout(B, L, choose_work_groups(L, params->work_groups));
   char *ws = static_cast<char *>(workspace);
 
   StepArgs a;
@@ -176,6 +151,7 @@ int museattn_attn_step_profiled(const void *qkv, const int32_t *positions, const
   a.wk = params->k_norm_w;
   a.wo = params->o_norm_w;
   a.qbuf = reinterpret_cast<float *>(ws + ly.q_off);
+  a.plan = reinterpret_cast<int *>(ws + ly.plan_off);
   a.part_ml = reinterpret_cast<float *>(ws + ly.ml_off);
   a.part_o = reinterpret_cast<float *>(ws + ly.o_off);
   a.num_rows = num_rows;
@@ -189,8 +165,7 @@ int museattn_attn_step_profiled(const void *qkv, const int32_t *positions, const
   a.max_seq_len = max_seq_len;
   a.page_size = page_size;
   a.sliding = layer_kind == MUSEATTN_SLIDING;
-  a.nsplit = ly.nsplit;
-  a.split_keys = ly.split;
+  a.work_groups = ly.work_groups;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();   // clear an error left by earlier, unrelated calls

@@ -46,12 +46,15 @@ __global__ __launch_bounds__(64) void prologue_kernel(StepArgs a) {
 
   const float wq = a.wq[d], wk = a.wk[d];
   const float inv64 = 1.0f / 64.0f;
+  // every load of the token first (one memory round trip), then the math
+  float x[HQ + 2 * HKV];
+#pragma unroll
+  for (int h = 0; h < HQ + 2 * HKV; ++h) x[h] = bf16_bits_to_f32(row[h * D + d]);
 
-#pragma unroll 4
+#pragma unroll
   for (int h = 0; h < HQ; ++h) {
-    const float x = bf16_bits_to_f32(row[h * D + d]);
-    const float ms = wave_sum(x * x) * inv64;
-    float y = x / sqrtf(ms + a.eps) * wq * a.q_scale;
+    const float ms = wave_sum(x[h] * x[h]) * inv64;
+    float y = x[h] / sqrtf(ms + a.eps) * wq * a.q_scale;
     if (a.sliding) {
       const float partner = __shfl_xor(y, 32, 64);
       y = y * c + sgn * partner * s;
@@ -64,16 +67,15 @@ __global__ __launch_bounds__(64) void prologue_kernel(StepArgs a) {
   uint8_t *vrow = a.v_cache + (uint64_t)r * ROW;
 #pragma unroll
   for (int g = 0; g < HKV; ++g) {
-    const float x = bf16_bits_to_f32(row[K_OFF + g * D + d]);
-    const float ms = wave_sum(x * x) * inv64;
-    float y = x / sqrtf(ms + a.eps) * wk;
+    const float xk = x[HQ + g];
+    const float ms = wave_sum(xk * xk) * inv64;
+    float y = xk / sqrtf(ms + a.eps) * wk;
     if (a.sliding) {
       const float partner = __shfl_xor(y, 32, 64);
       y = y * c + sgn * partner * s;
     }
     krow[g * D + d] = to_e4m3(y / a.kv_scale);
-    const float v = bf16_bits_to_f32(row[V_OFF + g * D + d]);
-    vrow[g * D + d] = to_e4m3(v / a.kv_scale);
+    vrow[g * D + d] = to_e4m3(x[HQ + HKV + g] / a.kv_scale);
   }
 }
 

@@ -34,12 +34,12 @@ def upload(w: W.Workload, dev="cuda:0", fill_all=None) -> dict:
                 out=torch.empty(w.B, w.L, 1024, dtype=torch.bfloat16, device=dev))
 
 
-def run(w: W.Workload, d: dict, split_keys=0, stream=None, workspace=None):
+def run(w: W.Workload, d: dict, work_groups=0, stream=None, workspace=None):
     P.attn_step(d["qkv"], d["positions"], d["table"], d["seq_lens"], d["k_cache"], d["v_cache"],
                 w.kv_scale, w.page_size, w.layer_kind, d["out"], stream,
                 q_norm_w=d["w_q"], k_norm_w=d["w_k"], o_norm_w=d["w_o"],
                 max_seq_len=w.max_seq_len, workspace=workspace, eps=EPS, q_scale=QS,
-                rope_base=ROPE_BASE, split_keys=split_keys)
+                rope_base=ROPE_BASE, work_groups=work_groups)
     return d["out"]
 
 

@@ -45,7 +45,7 @@ def _args(**kw):
         kw.get("page_size", 1), kw.get("layer_kind", P.FULL)
     params = P.make_params(kw.get("wq", A["wq"]), A["wk"], A["wo"], kw.get("eps", 1e-6),
                            kw.get("q_scale", 5.473), kw.get("rope_base", 1e4),
-                           kw.get("split_keys", 0))
+                           kw.get("work_groups", 0))
     need = P.lib().museattn_workspace_bytes(B, L, msl, ps if ps in (1, 64) else 1,
                                             kind if kind in (0, 1) else 0, ctypes.byref(params))
     return dict(qkv=kw.get("qkv", A["qkv"]), positions=A["pos"], table=A["table"],
@@ -65,7 +65,8 @@ def test_valid_arguments_pass():
     assert _check() == 0
     assert _check(page_size=64, table_stride=16, num_rows=64 * 100) == 0
     assert _check(L=8, layer_kind=P.SLIDING) == 0
-    assert _check(split_keys=4096) == 0
+    assert _check(work_groups=65535) == 0
+    assert _check(B=1024) == 0
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -77,7 +78,6 @@ def test_valid_arguments_pass():
     (dict(L=9), -4),
     (dict(L=0), -4),
     (dict(B=0), -4),
-    (dict(B=70000), -4),
     (dict(max_seq_len=0), -4),
     (dict(num_rows=0), -4),
     (dict(page_size=64, table_stride=100, num_rows=1000), -4),   # not a multiple of 64
@@ -91,22 +91,24 @@ def test_valid_arguments_pass():
     (dict(kv_scale=float("nan")), -8),
     (dict(eps=-1.0), -8),
     (dict(rope_base=0.0), -8),
-    (dict(split_keys=100), -8),
-    (dict(split_keys=8192), -8),
+    (dict(work_groups=-1), -8),
+    (dict(work_groups=65536), -8),
+    (dict(B=1025), -4),
     (dict(out=A["qkv"] + 4096), -9),
 ])
 def test_invalid_arguments_are_rejected(kw, status):
     assert _check(**kw) == status
 
 
-def test_workspace_and_split_schedule():
-    # decode at the large batch: ~2048 work-groups, splits multiple of 128
-    sk = P.split_keys(32, 1, 100001, P.FULL)
-    assert sk % 128 == 0 and 1024 <= sk <= 4096
+def test_workspace_and_launch_shape():
+    # decode: 2 work-groups per CU of MI355X; verify blocks: 1 per CU
+    assert P.work_groups(32, 1, 100001, P.FULL) == 512
+    assert P.work_groups(1, 8, 80008, P.SLIDING) == 256
+    assert P.work_groups(1, 8, 80008, P.FULL, work_groups=7) == 7
     n = P.workspace_bytes(32, 1, 100001, 1, P.FULL)
-    nsplit = -(-100001 // sk)
-    assert n >= 32 * 16 * 64 * 4 + 32 * 16 * nsplit * 66 * 4
-    # the sliding span is bounded by the window whatever the context
+    slots = 512 + 32
+    assert n >= 32 * 16 * 64 * 4 + 32 * 4 + slots * 16 * 66 * 4
+    # independent of the context length (the plan is made on the device)
     assert P.workspace_bytes(4, 8, 1 << 20, 1, P.SLIDING) == P.workspace_bytes(4, 8, 4096, 1, P.SLIDING)
     with pytest.raises(ValueError):
         P.workspace_bytes(1, 9, 100, 1, P.FULL)

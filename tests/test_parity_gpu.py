@@ -94,7 +94,7 @@ EDGE = [
 def test_edge_parity(case):
     name, B, L, ctx, kind, ps, kv = case
     w = W.make(name, 77, B, L, ctx, kind, ps, kv)
-    log(f"[edge] {name} ctx={w.ctx.tolist()[:6]} split={P.split_keys(B, L, w.max_seq_len, kind)}")
+    log(f"[edge] {name} ctx={w.ctx.tolist()[:6]} work-groups={P.work_groups(B, L, w.max_seq_len, kind)}")
     host = W.build_pools_numpy(w)
     d = upload(w)
     run(w, d)
@@ -116,14 +116,16 @@ def test_million_key_verify_block():
 
 # ----------------------------------------------------------- properties
 
-def test_split_count_invariance_and_determinism():
-    w = W.make("splits", 5, 3, 1, (3000, 9000), W.FULL, 1, 1.0)
+def test_partition_invariance_and_determinism():
+    """The work-group count changes only the summation order; one, a prime
+    number, and more work-groups than chunks (some then idle) all agree."""
+    w = W.make("partition", 5, 3, 1, (3000, 9000), W.FULL, 1, 1.0)
     host = W.build_pools_numpy(w)
     d = upload(w)
     outs = []
-    for sk in (32, 128, 320, 1024, 4096, 0):
-        log(f"[split] split_keys={sk}")
-        run(w, d, split_keys=sk)
+    for g in (1, 7, 64, 509, 4096, 0):
+        log(f"[partition] work_groups={g}")
+        run(w, d, work_groups=g)
         outs.append(d["out"].clone())
     torch.cuda.synchronize()
     full_check(w, d, host_pools=host)
@@ -134,18 +136,31 @@ def test_split_count_invariance_and_determinism():
     assert torch.equal(d["out"], outs[-1]), "two identical calls differ"
 
 
-def test_verify_split_invariance():
-    w = W.make("vsplits", 6, 2, 8, (2500, 4000), W.SLIDING, 1, 1.0)
+def test_verify_partition_invariance():
+    w = W.make("vpartition", 6, 2, 8, (2500, 4000), W.SLIDING, 1, 1.0)
     host = W.build_pools_numpy(w)
     d = upload(w)
     outs = []
-    for sk in (32, 96, 1024, 0):
-        run(w, d, split_keys=sk)
+    for g in (1, 3, 100, 1000, 0):
+        run(w, d, work_groups=g)
         outs.append(d["out"].clone())
     torch.cuda.synchronize()
     full_check(w, d, host_pools=host)
     for o in outs[:-1]:
         assert (o.float() - outs[-1].float()).abs().max().item() <= 1.6e-2
+
+
+def test_many_requests_sharing_work_groups():
+    """More requests than chunks per work-group: shares cross several request
+    boundaries, so segments, partial slots and the last-contributor merge are
+    all exercised (and some requests have a single chunk)."""
+    w = W.make("many-short", 21, 300, 1, (1, 90), W.FULL, 64, 1.0)
+    host = W.build_pools_numpy(w)
+    d = upload(w)
+    for g in (0, 97):
+        run(w, d, work_groups=g)
+        torch.cuda.synchronize()
+        full_check(w, d, host_pools=host)
 
 
 def test_page_size_does_not_change_the_result():
