@@ -21,13 +21,16 @@ __global__ __launch_bounds__(256) void combine_kernel(StepArgs a) {
   const int t = th / HQ, h = th % HQ;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int b = t / a.L, jt = t % a.L;
-  const int64_t p0 = a.plan[b], p1 = a.plan[b + 1], C = a.plan[a.B];
+  const int64_t p0 = a.plan[b], p1 = a.plan[b + 1];
   const int G = a.plan[a.B + 1];
-  // slots of request b: w + b for the work-groups w whose share meets its chunks
+  const int64_t Ct = (int64_t)a.plan[a.B] + (int64_t)a.B * a.seg_cost;
+  // slots of request b: w + b for the work-groups w whose cost share meets its
+  // chunks (chunk c of request b sits at cost p0 + (b + 1) * seg_cost + c)
   int s0 = 0, s1 = -1;
   if (p1 > p0) {
-    s0 = wg_of_chunk(p0, C, G) + b;
-    s1 = wg_of_chunk(p1 - 1, C, G) + b;
+    const int64_t q0 = p0 + (int64_t)(b + 1) * a.seg_cost;
+    s0 = wg_of_chunk(q0, Ct, G) + b;
+    s1 = wg_of_chunk(q0 + (p1 - p0) - 1, Ct, G) + b;
   }
   const float2 *ml = reinterpret_cast<const float2 *>(a.part_ml);
   const f32x4 *po = reinterpret_cast<const f32x4 *>(a.part_o);

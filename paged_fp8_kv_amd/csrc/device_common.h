@@ -15,7 +15,8 @@ constexpr int K_OFF = 1024, V_OFF = 1152, G_OFF = 1280;
 constexpr int ROW = 128;     // bytes of one cache row (2 KV heads x 64 E4M3 bytes)
 constexpr int WINDOW = 2048; // sliding window, the query's own position included
 constexpr int CHUNK = 32;    // keys per step of the attention kernel's inner loop
-constexpr int WAVES = 4;     // waves per attention work-group
+constexpr int WAVES = 8;     // waves per attention work-group (one work-group per CU)
+constexpr int THREADS = 64 * WAVES;
 constexpr int MAX_BATCH = 1024;   // requests per call (prefix sums live in LDS)
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -33,7 +34,6 @@ struct StepArgs {
   uint8_t *v_cache;
   uint16_t *out;           // bf16 bits [T][1024]
   const float *wq, *wk, *wo;
-  float *qbuf;             // [T][16][64] normed, rotated, scaled q
   int *plan;               // [B + 2]: chunk prefix sums of the requests, then the
                            // work-groups used (written by attention work-group 0)
   float *part_ml;          // [slot][L][16][2] (reference max in log2 units, sum)
@@ -43,6 +43,7 @@ struct StepArgs {
   int B, L, table_stride, max_seq_len, page_size, sliding;
   int work_groups;         // attention work-groups launched (each takes an equal
                            // share of all requests' key chunks)
+  int seg_cost;            // chunk-equivalents one segment start-up costs
 };
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t h) {
@@ -73,20 +74,23 @@ struct KeyRange {
   int klo, khi, kbase;
 };
 
-__device__ __forceinline__ KeyRange request_range(const StepArgs &a, int b) {
-  int sl = a.seq_lens[b];
+// The key range from a request's length and its first block token's position.
+__device__ __forceinline__ KeyRange range_from(const StepArgs &a, int sl, int p0) {
   sl = sl < 0 ? 0 : (sl > a.max_seq_len ? a.max_seq_len : sl);
   KeyRange r;
   r.khi = sl - 1;
   r.klo = 0;
   if (a.sliding) {
-    int p0 = a.positions[b * a.L];
     p0 = p0 < 0 ? 0 : (p0 > a.max_seq_len - 1 ? a.max_seq_len - 1 : p0);
     r.klo = p0 - (WINDOW - 1);
     r.klo = r.klo < 0 ? 0 : r.klo;
   }
   r.kbase = r.klo & ~(CHUNK - 1);
   return r;
+}
+
+__device__ __forceinline__ KeyRange request_range(const StepArgs &a, int b) {
+  return range_from(a, a.seq_lens[b], a.sliding ? a.positions[b * a.L] : 0);
 }
 
 // Chunks (of CHUNK keys, from kbase) that request b's key range spans.
@@ -113,7 +117,7 @@ __device__ __forceinline__ float wave_sum(float x) {
   return __int_as_float(q[0]) + __int_as_float(q[1]);
 }
 
-// Chunk c of C chunks spread over G work-groups (work-group w owns chunks
+// Cost unit c of C spread over G work-groups (work-group w owns units
 // [floor(w C / G), floor((w + 1) C / G))) belongs to work-group
 // floor(((c + 1) G - 1) / C).
 __device__ __forceinline__ int wg_of_chunk(int64_t c, int64_t C, int G) {

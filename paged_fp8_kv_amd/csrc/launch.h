@@ -4,7 +4,6 @@
 #include "device_common.h"
 
 namespace museattn {
-void launch_prologue(const StepArgs &a, hipStream_t stream);
 void launch_attn(const StepArgs &a, hipStream_t stream);
 void launch_combine(const StepArgs &a, hipStream_t stream);
 }  // namespace museattn

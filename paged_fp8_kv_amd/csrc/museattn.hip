@@ -1,6 +1,6 @@
 // Host side of libmuseattn: argument validation, the launch shape (a function
 // of host shapes only, so a call can be captured into a HIP graph), workspace
-// layout and the three launches.  See include/museattn.h for the contract.
+// layout and the two launches.  See include/museattn.h for the contract.
 #include <cmath>
 #include <cstdint>
 
@@ -17,27 +17,25 @@ constexpr int MAX_SEQ = 1 << 30;
 bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
 // Attention work-groups.  Each takes an equal share of all requests' key
-// chunks, so two per CU (the kernel's occupancy on MI355X's 256 CUs) keep
-// every CU busy to the end without a tail.  Verify blocks write 8x larger
-// partials, so they use one per CU.
+// chunks; one 8-wave work-group per CU of MI355X (256 CUs) keeps every CU
+// busy to the end without a tail.
 int choose_work_groups(int L, int requested) {
+  (void)L;
   if (requested > 0) return requested;
-  return L == 1 ? 512 : 256;
+  return 256;
 }
 
 struct Layout {
   int work_groups;
-  size_t q_off, plan_off, ml_off, o_off, total;
+  size_t plan_off, ml_off, o_off, total;
 };
 
 Layout layout(int B, int L, int work_groups) {
   Layout ly;
   ly.work_groups = work_groups;
-  const size_t T = (size_t)B * L;
   const size_t slots = (size_t)work_groups + B;   // partial slots w + b
   auto al = [](size_t x) { return (x + 255) / 256 * 256; };
-  ly.q_off = 0;
-  ly.plan_off = al(T * HQ * D * sizeof(float));
+  ly.plan_off = 0;
   ly.ml_off = ly.plan_off + al(((size_t)B + 2) * sizeof(int));
   ly.o_off = ly.ml_off + al(slots * L * HQ * 2 * sizeof(float));
   ly.total = ly.o_off + al(slots * L * HQ * D * sizeof(float));
@@ -150,7 +148,6 @@ int museattn_attn_step_profiled(const void *qkv, const int32_t *positions, const
   a.wq = params->q_norm_w;
   a.wk = params->k_norm_w;
   a.wo = params->o_norm_w;
-  a.qbuf = reinterpret_cast<float *>(ws + ly.q_off);
   a.plan = reinterpret_cast<int *>(ws + ly.plan_off);
   a.part_ml = reinterpret_cast<float *>(ws + ly.ml_off);
   a.part_o = reinterpret_cast<float *>(ws + ly.o_off);
@@ -166,10 +163,12 @@ int museattn_attn_step_profiled(const void *qkv, const int32_t *positions, const
   a.page_size = page_size;
   a.sliding = layer_kind == MUSEATTN_SLIDING;
   a.work_groups = ly.work_groups;
+  // a segment start-up (batch of loads + first rows) is worth about this many
+  // 32-key chunks of one work-group's streaming (measured on MI355X)
+  a.seg_cost = L == 1 ? 14 : 4;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();   // clear an error left by earlier, unrelated calls
-  launch_prologue(a, s);
   if (attn_start_event) (void)hipEventRecord(static_cast<hipEvent_t>(attn_start_event), s);
   launch_attn(a, s);
   if (attn_end_event) (void)hipEventRecord(static_cast<hipEvent_t>(attn_end_event), s);
