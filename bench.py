@@ -3,15 +3,16 @@
 Default workload: decode, batch 32, full-attention layer, per-request
 context drawn uniformly from [60000, 100000] (seed 1002), page size 1, random
 cache rows in ~80 GB of K+V pools, kv_scale 1.  A step is one museattn_attn_step
-call (prologue kernel, then the split-K attention kernel that also merges
-the partials and writes the gated output) over that batch with every input
-already resident in HBM.
+call (the attention kernel, which also normalises q and k and writes the new
+fp8 cache rows, then the combine kernel that merges the split-K partials and
+writes the gated output) over that batch with every input already resident in
+HBM.
 
 Prints ONE JSON line on stdout (progress goes to stderr):
   value       achieved HBM throughput of the step on the algorithmic K+V bytes
               (256 B per visible key), GB/s
-  roofline    the split-K attention kernel alone, timed with HIP events on the
-              stream it runs on, against MI355X's 8 TB/s
+  roofline    the attention kernel alone (the step's dominant kernel), timed
+              with HIP events on the stream it runs on, against MI355X's 8 TB/s
   cpu_baseline  the CPU oracle on a sample of the same workload
 """
 from __future__ import annotations
@@ -231,7 +232,7 @@ def main():
     traffic = read_traffic(kv)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": traffic, "kernel": "attn_kernel (split-K attention + merge + gated norm)",
+                "traffic": traffic, "kernel": "attn_kernel (q/k norm, cache write, split-K attention)",
                 "algorithmic_bytes_per_launch": kv, "avg_launch_us": round(attn_avg_ms * 1e3, 2)}
 
     cpu = None
