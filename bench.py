@@ -8,11 +8,18 @@ fp8 cache rows, then the combine kernel that merges the split-K partials and
 writes the gated output) over that batch with every input already resident in
 HBM.
 
+The timed region is one replay of a HIP graph holding the K steps (a decode
+loop runs its steps from captured graphs); --eager times K plain calls.
+
 Prints ONE JSON line on stdout (progress goes to stderr):
   value       achieved HBM throughput of the step on the algorithmic K+V bytes
               (256 B per visible key), GB/s
   roofline    the attention kernel alone (the step's dominant kernel), timed
               with HIP events on the stream it runs on, against MI355X's 8 TB/s
+  cold_cache_graph_replay  one-step graph replays, each after a 1 GiB read
+              flush: median, p10, p90, bootstrap 95% interval of the median,
+              and the replay time of a one-kernel graph (launch cost, not
+              subtracted)
   cpu_baseline  the CPU oracle on a sample of the same workload
 """
 from __future__ import annotations
@@ -21,7 +28,6 @@ import argparse
 import hashlib
 import json
 import os
-import statistics
 import sys
 import time
 
@@ -122,10 +128,12 @@ def main():
                     help="attention work-groups (0 = the library's choice)")
     ap.add_argument("--pool-rows", type=int, default=0,
                     help="override the pool size in rows (0 = the workload's own)")
-    ap.add_argument("--cold-reps", type=int, default=30,
+    ap.add_argument("--cold-reps", type=int, default=200,
                     help="graph replays timed one by one after a 1 GiB cache flush")
     ap.add_argument("--cpu-sample", type=int, default=16, help="requests the oracle times")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager", action="store_true",
+                    help="time K eager calls instead of one replay of K captured steps")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="run a 1 GiB device copy first (PMC calibration runs)")
     args = ap.parse_args()
@@ -136,6 +144,7 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
+    import numpy as np
     import torch
 
     import paged_fp8_kv_amd as P
@@ -184,15 +193,45 @@ def main():
         for e in pair:
             e.record()
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(evs[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+
+    def timed_eager():
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step(evs[i])
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0
+
+    mode = "eager"
+    if not args.eager:
+        # K steps captured into one HIP graph, as a decode loop runs them
+        steps_graph = torch.cuda.CUDAGraph()
+        cs = torch.cuda.Stream()
+        cs.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cs):
+            step()
+        torch.cuda.current_stream().wait_stream(cs)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(steps_graph):
+            for _ in range(args.steps):
+                step()
+        steps_graph.replay()           # untimed
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        steps_graph.replay()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        mode = "graph"
+    else:
+        wall = timed_eager()
     ms_per_step = wall * 1e3 / args.steps
-    attn_ms = [hip_elapsed_ms(s, e) for s, e in evs]
+    # the attention kernel's launch duration: HIP events recorded by the library
+    # on the kernel's stream around each launch, over K eager steps (event
+    # records captured inside a graph do not bracket the kernel on this runtime)
+    if mode == "graph":
+        timed_eager()
+    attn_ms = [hip_elapsed_ms(s0, e0) for s0, e0 in evs]
     attn_avg_ms = sum(attn_ms) / len(attn_ms)
-    log(f"timed {args.steps} steps: {ms_per_step * 1e3:.1f} us/step; attention kernel "
+    log(f"timed {args.steps} steps ({mode}): {ms_per_step * 1e3:.1f} us/step; attention kernel "
         f"avg {attn_avg_ms * 1e3:.1f} us (min {min(attn_ms) * 1e3:.1f})")
 
     cold = None
@@ -209,21 +248,40 @@ def main():
         torch.cuda.synchronize()
         with torch.cuda.graph(g):
             step()
-        times = []
-        for _ in range(args.cold_reps):
-            flush.sum()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            g.replay()
-            e1.record()
-            torch.cuda.synchronize()
-            times.append(e0.elapsed_time(e1) * 1e3)
-        times.sort()
-        cold = {"median_us": round(statistics.median(times), 2),
-                "p10_us": round(times[len(times) // 10], 2),
-                "p90_us": round(times[(len(times) * 9) // 10], 2), "reps": len(times)}
+        tiny = torch.zeros(1, device=dev)
+        g_tiny = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_tiny):
+            tiny.add_(1.0)
+
+        def replay_times(graph):
+            out_us = []
+            for _ in range(args.cold_reps):
+                flush.sum()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                graph.replay()
+                e1.record()
+                torch.cuda.synchronize()
+                out_us.append(e0.elapsed_time(e1) * 1e3)
+            return np.sort(np.array(out_us))
+
+        times = replay_times(g)
+        tiny_times = replay_times(g_tiny)
+        # bootstrap 95% interval of the median (seeded resampling)
+        rng = np.random.default_rng(0)
+        meds = np.median(rng.choice(times, size=(2000, times.size), replace=True), axis=1)
+        med = float(np.median(times))
+        cold = {"median_us": round(med, 2),
+                "p10_us": round(float(np.percentile(times, 10)), 2),
+                "p90_us": round(float(np.percentile(times, 90)), 2),
+                "median_ci95_us": [round(float(np.percentile(meds, 2.5)), 2),
+                                   round(float(np.percentile(meds, 97.5)), 2)],
+                "gbs_at_median": round(w.kv_bytes / (med * 1e-6) / 1e9, 1),
+                "reps": int(times.size),
+                "trivial_graph_median_us": round(float(np.median(tiny_times)), 2)}
         log(f"graph replay after a 1 GiB flush: median {cold['median_us']} us "
-            f"(p10 {cold['p10_us']}, p90 {cold['p90_us']})")
+            f"(p10 {cold['p10_us']}, p90 {cold['p90_us']}, 95% CI {cold['median_ci95_us']}); "
+            f"a one-kernel graph replays in {cold['trivial_graph_median_us']} us")
         del flush
 
     kv = w.kv_bytes
@@ -233,7 +291,8 @@ def main():
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": traffic, "kernel": "attn_kernel (q/k norm, cache write, split-K attention)",
-                "algorithmic_bytes_per_launch": kv, "avg_launch_us": round(attn_avg_ms * 1e3, 2)}
+                "algorithmic_bytes_per_launch": kv, "avg_launch_us": round(attn_avg_ms * 1e3, 2),
+                "avg_launch_us_from": f"HIP events around each of {args.steps} eager launches"}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -243,7 +302,7 @@ def main():
         "metric": "us/step and achieved HBM GB/s (% peak), decode-32 full-attn ctx 80K, 1 GPU",
         "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
-        "us_per_step": round(ms_per_step * 1e3, 2), "pct_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "us_per_step": round(ms_per_step * 1e3, 2), "timing": mode, "pct_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "kv_dtype": "fp8_e4m3fn", "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "L": w.L, "layer": "full" if w.layer_kind == 0

@@ -385,6 +385,8 @@ struct Lds {
   float sm_l[WAVES][HQ];
   int pref[MAX_BATCH + 1];
   int scan[THREADS];
+  int req_len[MAX_BATCH];    // seq_lens[b], kept from the plan
+  int req_p0[MAX_BATCH];     // positions[b * L] (sliding layers)
 };
 
 // One segment: chunks [x, y) of request b's key range (chunk i = keys
@@ -606,6 +608,8 @@ __global__ __launch_bounds__(THREADS, 2) void attn_kernel(StepArgs a) {
     for (int k = 0; k < RPT; ++k) {
       cnt[k] = RPT * tid + k < a.B ? request_chunks(range_from(a, sl[k], p0[k])) : 0;
       sum += cnt[k];
+      sh.req_len[RPT * tid + k] = sl[k];
+      sh.req_p0[RPT * tid + k] = p0[k];
     }
   }
   sh.scan[tid] = sum;
@@ -658,7 +662,7 @@ __global__ __launch_bounds__(THREADS, 2) void attn_kernel(StepArgs a) {
     const int x = (int)(xs > 0 ? xs : 0);
     const int y = (int)(ys < nb ? ys : nb);
     if (y <= x) continue;
-    const KeyRange r = request_range(a, b);
+    const KeyRange r = range_from(a, sh.req_len[b], sh.req_p0[b]);
     process_segment<MODE, NT, NBUF>(a, b, r, x, y, w + b, sh);
   }
 }

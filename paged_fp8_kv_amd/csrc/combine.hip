@@ -4,18 +4,19 @@
 // (task page "Gated attention decode", section "What to compute", last line
 // of the listing; output shape from the same section).
 //
-// One 256-thread work-group per (token, head): 16 slot lanes x 16 dimension
-// quads accumulate the rescaled partials with independent loads, LDS sums the
-// slot lanes, and one wave finishes the gated norm.
+// One 256-thread work-group per (token, head).  The plan entries, the gate
+// and the output-norm weight are loaded as one batch; then 16 slot lanes x 16
+// dimension quads each merge their slots online (running max, rescaled sum
+// and output), so the partials take a single memory round trip; LDS merges
+// the 16 slot lanes and one wave finishes the gated norm.
 #include "device_common.h"
 #include "launch.h"
 
 namespace museattn {
 
 __global__ __launch_bounds__(256) void combine_kernel(StepArgs a) {
-  __shared__ float sm_max[4];
+  __shared__ float sm_m[16], sm_l[16];
   __shared__ __attribute__((aligned(16))) float sm_o[16][D];
-  __shared__ float sm_l[16];
 
   const int th = blockIdx.x;          // t * 16 + h
   const int t = th / HQ, h = th % HQ;
@@ -24,6 +25,8 @@ __global__ __launch_bounds__(256) void combine_kernel(StepArgs a) {
   const int64_t p0 = a.plan[b], p1 = a.plan[b + 1];
   const int G = a.plan[a.B + 1];
   const int64_t Ct = (int64_t)a.plan[a.B] + (int64_t)a.B * a.seg_cost;
+  const float g = bf16_bits_to_f32(a.qkv[(size_t)t * QKV_W + G_OFF + h * D + lane]);
+  const float wo = a.wo[lane];
   // slots of request b: w + b for the work-groups w whose cost share meets its
   // chunks (chunk c of request b sits at cost p0 + (b + 1) * seg_cost + c)
   int s0 = 0, s1 = -1;
@@ -36,42 +39,59 @@ __global__ __launch_bounds__(256) void combine_kernel(StepArgs a) {
   const f32x4 *po = reinterpret_cast<const f32x4 *>(a.part_o);
   auto entry = [&](int s) { return ((size_t)s * a.L + jt) * HQ + h; };
 
-  float m = -INFINITY;
-  for (int s = s0 + tid; s <= s1; s += 256) m = fmaxf(m, ml[entry(s)].x);
-  m = wave_max(m);
-  if (lane == 0) sm_max[wave] = m;
-  __syncthreads();
-  const float M = fmaxf(fmaxf(sm_max[0], sm_max[1]), fmaxf(sm_max[2], sm_max[3]));
-
+  // online merge of slots s0 + sl, s0 + sl + 16, ... (four loads in flight)
   const int sl = tid >> 4, dq = tid & 15;
+  float m = -INFINITY, l = 0.0f;
   f32x4 o = {0.f, 0.f, 0.f, 0.f};
-  float l = 0.0f;
-  if (M != -INFINITY) {
-#pragma unroll 4
-    for (int s = s0 + sl; s <= s1; s += 16) {
-      const size_t e = entry(s);
-      const float2 v = ml[e];
-      const float sc = v.x == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(v.x - M);
-      l += sc * v.y;
-      o += sc * po[e * (D / 4) + dq];
+  auto merge = [&](float2 v, f32x4 x) {
+    const float mn = fmaxf(m, v.x);
+    const float c0 = m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m - mn);
+    const float c1 = v.x == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(v.x - mn);
+    l = l * c0 + v.y * c1;
+    o = o * c0 + x * c1;
+    m = mn;
+  };
+  int s = s0 + sl;
+  for (; s + 48 <= s1; s += 64) {
+    float2 v[4];
+    f32x4 x[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const size_t e = entry(s + 16 * k);
+      v[k] = ml[e];
+      x[k] = po[e * (D / 4) + dq];
     }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) merge(v[k], x[k]);
+  }
+  for (; s <= s1; s += 16) {
+    const size_t e = entry(s);
+    merge(ml[e], po[e * (D / 4) + dq]);
   }
   *reinterpret_cast<f32x4 *>(&sm_o[sl][4 * dq]) = o;
-  if (dq == 0) sm_l[sl] = l;
+  if (dq == 0) {
+    sm_m[sl] = m;
+    sm_l[sl] = l;
+  }
   __syncthreads();
 
   if (wave == 0) {
     const int d = lane;
-    float od = 0.0f, lsum = 0.0f;
+    float M = -INFINITY;
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      od += sm_o[k][d];
-      lsum += sm_l[k];
+    for (int k = 0; k < 16; ++k) M = fmaxf(M, sm_m[k]);
+    float od = 0.0f, lsum = 0.0f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const float c = sm_m[k] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(sm_m[k] - M);
+        od += c * sm_o[k][d];
+        lsum += c * sm_l[k];
+      }
     }
     const float av = lsum > 0.0f ? od / lsum * a.kv_scale : 0.0f;
     const float ms2 = wave_sum(av * av) * (1.0f / 64.0f);
-    const float y = av / sqrtf(ms2 + a.eps) * a.wo[d];
-    const float g = bf16_bits_to_f32(a.qkv[(size_t)t * QKV_W + G_OFF + h * D + d]);
+    const float y = av / sqrtf(ms2 + a.eps) * wo;
     a.out[(size_t)t * (HQ * D) + h * D + d] = f32_to_bf16_bits(y / (1.0f + expf(-g)));
   }
 }

@@ -89,10 +89,6 @@ __device__ __forceinline__ KeyRange range_from(const StepArgs &a, int sl, int p0
   return r;
 }
 
-__device__ __forceinline__ KeyRange request_range(const StepArgs &a, int b) {
-  return range_from(a, a.seq_lens[b], a.sliding ? a.positions[b * a.L] : 0);
-}
-
 // Chunks (of CHUNK keys, from kbase) that request b's key range spans.
 __device__ __forceinline__ int request_chunks(const KeyRange &r) {
   return r.khi < r.klo ? 0 : (r.khi + 1 - r.kbase + CHUNK - 1) / CHUNK;
