@@ -6,7 +6,7 @@
 // chunks (see attn_kernel) and write one partial (reference max, sum,
 // unnormalised output) per (token, head) and segment; combine.hip merges them.
 //
-// Data path per 32-key chunk (one wave):
+// Decode data path per 32-key chunk (one wave):
 //  * cache rows come from an LDS copy of the split's table entries, so the
 //    dependent index load never stalls the row loads;
 //  * K rows: lane (n = lane%16, j = lane/16) loads 16 B of key n's row at
@@ -27,9 +27,9 @@
 // One 8-wave work-group per CU: two work-groups sharing a CU progress at
 // unequal rates (the older one wins issue arbitration), so the younger one
 // would finish alone.  Decode (L = 1): the 8 waves take interleaved chunks of
-// a segment and merge their states in LDS.  Verify (L > 1): wave w owns block
-// token w and walks every chunk of the segment (the re-reads of a row by the
-// 8 waves hit the cache).
+// a segment and merge their states in LDS.  Verify (L >= 2): the 8 tokens x 8
+// heads of a KV group form a dense 64-column contraction (see the verify
+// section below); waves split the KV heads, the column tiles and the chunks.
 #include "device_common.h"
 #include "launch.h"
 
@@ -200,6 +200,125 @@ __device__ __forceinline__ void compute_chunk(const RowBuf &rb, int u0, int j,
   }
 }
 
+// Verify blocks (L >= 2): a dense contraction per KV head.  The 64 columns of
+// Q_g^T are (token, head) pairs, column tile ct = tokens 2ct and 2ct + 1 x the
+// group's 8 heads (lane column n = token 2ct + n/8, head 8g + n%8).  Wave w
+// works on KV head g = w % 2, column tiles 2h and 2h + 1 of half h = (w/2) % 2,
+// and every other chunk starting at w / 4.  Per 32-key chunk:
+//  * K_g rows: lane (n, j) loads 16 B at byte 64g + 16j of key 16t + n (key
+//    tile t); K-step kk takes its half kk, dims 16j + 8kk + i, as for decode;
+//  * S^T (32 keys x 64 columns) = 2 key tiles x 4 column tiles x 2 K-steps,
+//    q as bf16 hi + lo;
+//  * V_g^T: lane (n, j) loads 4 B (dims 4n..4n+3 of KV head g) of the 8 keys
+//    it holds P for; a 4x4 byte transpose of each 4 keys turns them into 4
+//    M-tiles, M-tile dt row n = dim 4n + dt, so O^T tile (dt, ct) row 4j + r
+//    is dim 16j + 4r + dt;
+//  * the online softmax runs per column exactly as for decode.
+struct RowBuf2 {
+  uint4 k[2];      // key tile t: 16 B of KV head g's half row
+  uint32_t v[8];   // 4 B of V rows of the 8 keys this lane holds P for
+};
+
+struct VerifyState {
+  f32x4 o[4][2];   // [dim tile][column tile of the wave's half]
+  float m[2], l[2];
+  int lo[2], hi[2];   // visible key range of the lane's column's token
+};
+
+// Q_g^T operands of one KV head in LDS, shared by that head's 4 waves:
+// [column tile][K-step][hi, lo][lane].
+struct VerifyQ {
+  bf16x8 op[4][2][2][64];
+};
+
+__device__ __forceinline__ void load_rows2(RowBuf2 &rb, const uint8_t *__restrict__ kc,
+                                           const uint8_t *__restrict__ vc, const uint32_t *lrows,
+                                           int n, int j, int g) {
+  const uint32_t k0 = lrows[n];
+  const uint32_t k1 = lrows[16 + n];
+  const uint4 va = *reinterpret_cast<const uint4 *>(lrows + 4 * j);
+  const uint4 vb = *reinterpret_cast<const uint4 *>(lrows + 16 + 4 * j);
+  rb.k[0] = *reinterpret_cast<const uint4 *>(kc + (uint64_t)k0 * ROW + 64 * g + 16 * j);
+  rb.k[1] = *reinterpret_cast<const uint4 *>(kc + (uint64_t)k1 * ROW + 64 * g + 16 * j);
+  const uint32_t vr[8] = {va.x, va.y, va.z, va.w, vb.x, vb.y, vb.z, vb.w};
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    rb.v[i] = *reinterpret_cast<const uint32_t *>(vc + (uint64_t)vr[i] * ROW + 64 * g + 4 * n);
+}
+
+__device__ __forceinline__ void compute_chunk2(const RowBuf2 &rb, int u0, int lane, int half,
+                                               int nct, VerifyState &st, const VerifyQ &q) {
+  const int j = lane >> 4;
+  bf16x8 ka[2][2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    ka[t][0] = fp8x8_to_bf16(rb.k[t].x, rb.k[t].y);
+    ka[t][1] = fp8x8_to_bf16(rb.k[t].z, rb.k[t].w);
+  }
+  uint32_t ty[4], tz[4];
+  transpose4x4(rb.v[0], rb.v[1], rb.v[2], rb.v[3], ty[0], ty[1], ty[2], ty[3]);
+  transpose4x4(rb.v[4], rb.v[5], rb.v[6], rb.v[7], tz[0], tz[1], tz[2], tz[3]);
+  bf16x8 va[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) va[dt] = fp8x8_to_bf16(ty[dt], tz[dt]);
+
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const int ct = 2 * half + c;
+    if (ct >= nct) break;   // uniform
+    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const bf16x8 qh = q.op[ct][kk][0][lane], ql = q.op[ct][kk][1][lane];
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[0][kk], qh, s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[1][kk], qh, s1, 0, 0, 0);
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[0][kk], ql, s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[1][kk], ql, s1, 0, 0, 0);
+    }
+    float sc[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+    const int lo = st.lo[c], hi = st.hi[c];
+    if (u0 < lo || u0 + CHUNK - 1 > hi) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int u = u0 + (i >> 2) * 16 + 4 * j + (i & 3);
+        if (u < lo || u > hi) sc[i] = -INFINITY;
+      }
+    }
+    float cmax = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
+                       fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
+    cmax = head_max(cmax);
+    if (__any(cmax > st.m[c] + RESCALE_SLACK)) {
+      const float mnew = fmaxf(st.m[c], cmax);
+      const float alpha = mnew == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(st.m[c] - mnew);
+      st.l[c] *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) st.o[dt][c] *= alpha;
+      st.m[c] = mnew;
+    }
+    const float muse = st.m[c] == -INFINITY ? 0.0f : st.m[c];
+    float pv[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      pv[i] = __builtin_amdgcn_exp2f(sc[i] - muse);
+      st.l[c] += pv[i];
+    }
+    bf16x8 ph, pl;
+#pragma unroll
+    for (int i = 0; i < 8; i += 2) {
+      const f32x2 f = {pv[i], pv[i + 1]};
+      const bf16x2 h = __builtin_convertvector(f, bf16x2);
+      const bf16x2 r = __builtin_convertvector(f - __builtin_convertvector(h, f32x2), bf16x2);
+      ph[i] = h[0]; ph[i + 1] = h[1];
+      pl[i] = r[0]; pl[i + 1] = r[1];
+    }
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      st.o[dt][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[dt], ph, st.o[dt][c], 0, 0, 0);
+      st.o[dt][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[dt], pl, st.o[dt][c], 0, 0, 0);
+    }
+  }
+}
+
 // E4M3FN byte of x (OCP format: bias 7, max 448, no infinities), round to
 // nearest even, saturating.  The gfx950 converter rounds to nearest even but
 // turns magnitudes past the last rounding interval into NaN, so values are
@@ -223,25 +342,23 @@ __device__ __forceinline__ float2 rope_cs(float rope_base, int p, int i) {
   return make_float2((float)cd, (float)sd);
 }
 
-// Split and QK-norm of token t's query, RoPE on sliding layers, and the B
-// operand of S^T = K . Q^T (task page "Gated attention decode", section "What
-// to compute", first three lines of the listing).  Lane (n, j) owns dims
-// 16j..16j+15 of head n: the head's rmsnorm is a sum over its 4 lanes, the
-// RoPE partner (dim +-32) sits in lane (n, j ^ 2) = lane ^ 32.  K-step kk of
-// the operand holds q[16j + 8(kk%2) + i] (i < 8) when head n belongs to KV
-// head kk/2, else 0; q (times log2(e)/8 and kv_scale) is split into bf16
-// hi + lo.  cs: the token's 32 (cos, sin) pairs in LDS (sliding only).
+// Split and QK-norm of one (token, head) query and RoPE on sliding layers
+// (task page "Gated attention decode", section "What to compute", first three
+// lines of the listing).  Lane (n, j) holds dims 16j..16j+15: the head's
+// rmsnorm is a sum over its 4 lanes (n, n+16, n+32, n+48), and the RoPE
+// partner (dim +-32) sits in lane (n, j ^ 2) = lane ^ 32.  y = rmsnorm(q) *
+// w_q * q_scale, rotated.  cs: the token's 32 (cos, sin) pairs in LDS.
 struct QIn {
   uint4 r0, r1;   // the lane's 16 bf16 values of q
 };
 
-__device__ __forceinline__ QIn load_q_in(const StepArgs &a, int t, int n, int j) {
-  const uint16_t *src = a.qkv + (size_t)t * QKV_W + n * D + 16 * j;
+__device__ __forceinline__ QIn load_q_in(const StepArgs &a, int t, int head, int j) {
+  const uint16_t *src = a.qkv + (size_t)t * QKV_W + head * D + 16 * j;
   return QIn{*reinterpret_cast<const uint4 *>(src), *reinterpret_cast<const uint4 *>(src + 8)};
 }
 
-__device__ __forceinline__ void make_q(const StepArgs &a, const QIn &in, const f32x4 (&wv)[4],
-                                       int j, int n, float qmul, const float2 *cs, QOps &qo) {
+__device__ __forceinline__ void q_values(const StepArgs &a, const QIn &in, const f32x4 (&wv)[4],
+                                         int j, const float2 *cs, float (&y)[16]) {
   const uint32_t raw[8] = {in.r0.x, in.r0.y, in.r0.z, in.r0.w, in.r1.x, in.r1.y, in.r1.z, in.r1.w};
   float x[16];
 #pragma unroll
@@ -254,7 +371,6 @@ __device__ __forceinline__ void make_q(const StepArgs &a, const QIn &in, const f
   for (int k = 0; k < 16; ++k) ss += x[k] * x[k];
   const float ms = head_sum(ss) * (1.0f / 64.0f);
   const float den = sqrtf(ms + a.eps);
-  float y[16];
 #pragma unroll
   for (int k = 0; k < 16; ++k) y[k] = x[k] / den * wv[k >> 2][k & 3] * a.q_scale;
   if (a.sliding) {
@@ -268,18 +384,32 @@ __device__ __forceinline__ void make_q(const StepArgs &a, const QIn &in, const f
       y[k] = low ? y[k] * c.x - partner * c.y : y[k] * c.x + partner * c.y;
     }
   }
+}
+
+// One K-step of the B operand of S^T = K . Q^T: q[16j + 8 half + i] * mul
+// (i < 8), split into bf16 hi + lo.
+__device__ __forceinline__ void pack_q(const float (&y)[16], int half, float mul, bf16x8 &hi,
+                                       bf16x8 &lo) {
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) {
-    const float mul = (n >> 3) == (kk >> 1) ? qmul : 0.0f;
-#pragma unroll
-    for (int i = 0; i < 8; i += 2) {
-      const f32x2 f = {y[8 * (kk & 1) + i] * mul, y[8 * (kk & 1) + i + 1] * mul};
-      const bf16x2 h = __builtin_convertvector(f, bf16x2);
-      const bf16x2 l = __builtin_convertvector(f - __builtin_convertvector(h, f32x2), bf16x2);
-      qo.hi[kk][i] = h[0]; qo.hi[kk][i + 1] = h[1];
-      qo.lo[kk][i] = l[0]; qo.lo[kk][i + 1] = l[1];
-    }
+  for (int i = 0; i < 8; i += 2) {
+    const f32x2 f = {y[8 * half + i] * mul, y[8 * half + i + 1] * mul};
+    const bf16x2 h = __builtin_convertvector(f, bf16x2);
+    const bf16x2 l = __builtin_convertvector(f - __builtin_convertvector(h, f32x2), bf16x2);
+    hi[i] = h[0]; hi[i + 1] = h[1];
+    lo[i] = l[0]; lo[i + 1] = l[1];
   }
+}
+
+// Decode: head n's column of the block-diagonal Q^T.  K-step kk covers KV head
+// kk/2, so it holds head n's values when n/8 == kk/2 and zeros otherwise; q is
+// multiplied by log2(e)/8 and kv_scale (qmul).
+__device__ __forceinline__ void make_q(const StepArgs &a, const QIn &in, const f32x4 (&wv)[4],
+                                       int j, int n, float qmul, const float2 *cs, QOps &qo) {
+  float y[16];
+  q_values(a, in, wv, j, cs, y);
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk)
+    pack_q(y, kk & 1, (n >> 3) == (kk >> 1) ? qmul : 0.0f, qo.hi[kk], qo.lo[kk]);
 }
 
 // The new k and v rows of the block tokens flagged in `own` (bit jt = token
@@ -341,6 +471,9 @@ __device__ __forceinline__ void write_new_rows(const StepArgs &a, int b, unsigne
 #ifndef MUSEATTN_DECODE_NBUF
 #define MUSEATTN_DECODE_NBUF 2
 #endif
+#ifndef MUSEATTN_VERIFY_NBUF
+#define MUSEATTN_VERIFY_NBUF 2
+#endif
 
 constexpr int PIECE_CHUNKS = MAX_SPLIT_LDS / CHUNK;   // chunks whose rows one LDS fill holds
 
@@ -380,7 +513,12 @@ __device__ __forceinline__ void store_table(const StepArgs &a, const TableIn &in
 struct Lds {
   uint32_t lrows[MAX_SPLIT_LDS];
   float2 cs[8][32];          // RoPE (cos, sin) per block token and pair
-  float sm_o[WAVES][HQ][D];
+  union {
+    float sm_o[WAVES][HQ][D];   // decode: the 8 waves' O per head
+    float mrg[2][64][68];       // verify merge: chunk lane 1's O per KV head and column (padded)
+    VerifyQ vq[2];              // verify chunk loop: Q^T operands per KV head
+  };
+  float mrg_ml[2][64][2];       // verify merge: its (max, sum) per column
   float sm_m[WAVES][HQ];
   float sm_l[WAVES][HQ];
   int pref[MAX_BATCH + 1];
@@ -391,8 +529,10 @@ struct Lds {
 
 // One segment: chunks [x, y) of request b's key range (chunk i = keys
 // kbase + 32i ..), processed by the whole work-group, leaving one partial per
-// (token, head) in slot `slot`.
-template <int MODE, int NT, int NBUF>
+// (token, head) in slot `slot`.  MODE 0: decode (L = 1), the 8 waves take
+// interleaved chunks and both KV heads.  MODE 2: verify (L >= 2), wave w takes
+// KV head w % 2, column half (w / 2) % 2 and every other chunk from w / 4.
+template <int MODE, int NBUF>
 __device__ __forceinline__ void process_segment(const StepArgs &a, int b, const KeyRange &r, int x,
                                                 int y, int slot, Lds &sh) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -401,6 +541,10 @@ __device__ __forceinline__ void process_segment(const StepArgs &a, int b, const 
   const int nseg = y - x;
   const int npieces = (nseg + PIECE_CHUNKS - 1) / PIECE_CHUNKS;
   auto piece_x = [&](int pc) { return x + (int)((int64_t)pc * nseg / npieces); };
+  const int g = wave & 1;                  // verify: the wave's KV head,
+  const int half = (wave >> 1) & 1;        // column half (column tiles 2 half, 2 half + 1)
+  const int cl = wave >> 2;                // and chunk lane
+  const int nct = (a.L + 1) >> 1;          // verify: live column tiles
 
   // One batch of loads for everything the segment starts with: positions, the
   // first piece's table entries, the tokens' q rows and norm weights, and the
@@ -408,46 +552,70 @@ __device__ __forceinline__ void process_segment(const StepArgs &a, int b, const 
   int pos[8];
 #pragma unroll
   for (int jt = 0; jt < 8; ++jt) pos[jt] = a.positions[b * a.L + (jt < a.L ? jt : a.L - 1)];
+  int cpos[2];   // verify: position of the token of the lane's column, per column tile
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const int tk = 2 * (2 * half + c) + (n >> 3);
+    cpos[c] = MODE == 0 ? 0 : a.positions[b * a.L + (tk < a.L ? tk : a.L - 1)];
+  }
   TableIn tin;
   load_table_in(a, b, r, r.kbase + x * CHUNK, tin);
-  QIn qin[NT];
-#pragma unroll
-  for (int tk = 0; tk < NT; ++tk) {
-    const int jt = MODE == 0 ? 0 : wave + WAVES * tk;
-    qin[tk] = load_q_in(a, b * a.L + (jt < a.L ? jt : 0), n, j);
-  }
+  // decode: head n of the token; verify: column tile 2 half + cl of KV head g
+  const int qct = 2 * half + cl;
+  const int qtk = MODE == 0 ? 0 : 2 * qct + (n >> 3);
+  const QIn qin = load_q_in(a, b * a.L + (qtk < a.L ? qtk : a.L - 1),
+                            MODE == 0 ? n : 8 * g + (n & 7), j);
   const f32x4 *w4 = reinterpret_cast<const f32x4 *>(a.wq + 16 * j);
   const f32x4 wv[4] = {w4[0], w4[1], w4[2], w4[3]};
   const RowIn rin = load_row_in(a, b);
   __builtin_amdgcn_sched_barrier(0);
 
-  __syncthreads();   // the previous segment is done with sh.cs and sh.lrows
+  __syncthreads();   // the previous segment is done with sh.cs, sh.lrows and the merge buffers
   if (a.sliding) {
     if (tid < a.L * 32) sh.cs[tid >> 5][tid & 31] = rope_cs(a.rope_base, a.positions[b * a.L + (tid >> 5)], tid & 31);
     __syncthreads();
   }
   store_table(a, tin, sh.lrows);
-  TokState ts[NT];
-  QOps qo[NT];
+
+  // per-token key ranges: the causal bound is the token's position p, the
+  // window (sliding layers) starts 2047 keys before it
+  auto token_range = [&](bool live, int p, int &lo, int &hi) {
+    hi = live ? (p < r.khi ? p : r.khi) : -1;
+    lo = a.sliding ? p - (WINDOW - 1) : 0;
+  };
+  TokState ts[1];
+  QOps qo[1];
+  VerifyState vs;
+  if constexpr (MODE == 0) {
+    token_range(true, pos[0], ts[0].lo, ts[0].hi);
+    ts[0].live = true;
+    ts[0].m = -INFINITY;
+    ts[0].l = 0.0f;
 #pragma unroll
-  for (int tk = 0; tk < NT; ++tk) {
-    const int jt = MODE == 0 ? 0 : wave + WAVES * tk;
-    ts[tk].live = jt < a.L;
-    const int jq = ts[tk].live ? jt : 0;
-    int p = pos[0];
+    for (int mt = 0; mt < 8; ++mt) ts[0].o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    make_q(a, qin, wv, j, n, qmul, sh.cs[0], qo[0]);
+  } else {
 #pragma unroll
-    for (int k = 1; k < 8; ++k) p = jq == k ? pos[k] : p;
-    ts[tk].hi = p < r.khi ? p : r.khi;
-    ts[tk].lo = a.sliding ? p - (WINDOW - 1) : 0;
-    ts[tk].m = -INFINITY;
-    ts[tk].l = 0.0f;
+    for (int c = 0; c < 2; ++c) {
+      token_range(2 * (2 * half + c) + (n >> 3) < a.L, cpos[c], vs.lo[c], vs.hi[c]);
+      vs.m[c] = -INFINITY;
+      vs.l[c] = 0.0f;
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt) ts[tk].o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    make_q(a, qin[tk], wv, j, n, qmul, sh.cs[jq], qo[tk]);
+      for (int dt = 0; dt < 4; ++dt) vs.o[dt][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    const int ct = qct;
+    if (ct < nct) {   // uniform
+      float yq[16];
+      q_values(a, qin, wv, j, sh.cs[qtk < a.L ? qtk : a.L - 1], yq);
+      bf16x8 h0, l0, h1, l1;
+      pack_q(yq, 0, qmul, h0, l0);
+      pack_q(yq, 1, qmul, h1, l1);
+      sh.vq[g].op[ct][0][0][lane] = h0;
+      sh.vq[g].op[ct][0][1][lane] = l0;
+      sh.vq[g].op[ct][1][0][lane] = h1;
+      sh.vq[g].op[ct][1][1][lane] = l1;
+    }
   }
-  bool any_live = false;
-#pragma unroll
-  for (int tk = 0; tk < NT; ++tk) any_live |= ts[tk].live;
   // New rows of the block tokens whose key falls in this segment: only this
   // work-group reads them, so a workgroup release before the barrier orders
   // the writes before its own loads.
@@ -480,40 +648,57 @@ __device__ __forceinline__ void process_segment(const StepArgs &a, int b, const 
     // the steady state every load is unconditional -- chunk indices past the
     // end are clamped to the last chunk -- so the compiler can count the loads
     // in flight and wait only for the buffer it is about to use.
-    const int c0 = MODE == 0 ? wave : 0;
-    const int cstep = MODE == 0 ? WAVES : 1;
+    const int c0 = MODE == 0 ? wave : cl;
+    const int cstep = MODE == 0 ? WAVES : 2;
     const int nloc = nchunks > c0 ? (nchunks - c0 + cstep - 1) / cstep : 0;
-    if (any_live && nloc > 0) {
+    if (nloc > 0) {
       const int last = nloc - 1;
-      RowBuf buf[NBUF];
+      auto rows_of = [&](int i) { return sh.lrows + (c0 + i * cstep) * CHUNK; };
+      auto key_of = [&](int i) { return kstart + (c0 + i * cstep) * CHUNK; };
+      if constexpr (MODE == 0) {
+        RowBuf buf[NBUF];
 #pragma unroll
-      for (int k = 0; k < NBUF; ++k) {
-        const int i = k < last ? k : last;
-        load_rows(buf[k], a.k_cache, a.v_cache, sh.lrows + (c0 + i * cstep) * CHUNK, n, j);
-      }
-      int i = 0;
-      for (; i + NBUF <= nloc; i += NBUF) {
+        for (int k = 0; k < NBUF; ++k)
+          load_rows(buf[k], a.k_cache, a.v_cache, rows_of(k < last ? k : last), n, j);
+        int i = 0;
+        for (; i + NBUF <= nloc; i += NBUF) {
 #pragma unroll
-        for (int k = 0; k < NBUF; ++k) {
-          compute_chunk<NT>(buf[k], kstart + (c0 + (i + k) * cstep) * CHUNK, j, ts, qo);
-          int inext = i + k + NBUF;
-          inext = inext < last ? inext : last;
-          load_rows(buf[k], a.k_cache, a.v_cache, sh.lrows + (c0 + inext * cstep) * CHUNK, n, j);
+          for (int k = 0; k < NBUF; ++k) {
+            compute_chunk<1>(buf[k], key_of(i + k), j, ts, qo);
+            const int inext = i + k + NBUF;
+            load_rows(buf[k], a.k_cache, a.v_cache, rows_of(inext < last ? inext : last), n, j);
+          }
         }
-      }
 #pragma unroll
-      for (int k = 0; k < NBUF - 1; ++k)
-        if (i + k < nloc)
-          compute_chunk<NT>(buf[k], kstart + (c0 + (i + k) * cstep) * CHUNK, j, ts, qo);
+        for (int k = 0; k < NBUF - 1; ++k)
+          if (i + k < nloc) compute_chunk<1>(buf[k], key_of(i + k), j, ts, qo);
+      } else {
+        RowBuf2 buf[NBUF];
+#pragma unroll
+        for (int k = 0; k < NBUF; ++k)
+          load_rows2(buf[k], a.k_cache, a.v_cache, rows_of(k < last ? k : last), n, j, g);
+        int i = 0;
+        for (; i + NBUF <= nloc; i += NBUF) {
+#pragma unroll
+          for (int k = 0; k < NBUF; ++k) {
+            compute_chunk2(buf[k], key_of(i + k), lane, half, nct, vs, sh.vq[g]);
+            const int inext = i + k + NBUF;
+            load_rows2(buf[k], a.k_cache, a.v_cache, rows_of(inext < last ? inext : last), n, j, g);
+          }
+        }
+#pragma unroll
+        for (int k = 0; k < NBUF - 1; ++k)
+          if (i + k < nloc) compute_chunk2(buf[k], key_of(i + k), lane, half, nct, vs, sh.vq[g]);
+      }
     }
   }
 
-  // Lane (n, j) holds O^T of head n at V-row bytes 8(4j + r) + mt, r < 4: KV head
-  // j/2, dims 32(j%2) + 8r + mt.  Only lanes whose KV head is head n's own hold
-  // meaningful values.
-  const bool own = (j >> 1) == (n >> 3);
-  const int dbase = 32 * (j & 1);
-  if (MODE == 0) {
+  if constexpr (MODE == 0) {
+    // Lane (n, j) holds O^T of head n at V-row bytes 8(4j + r) + mt, r < 4: KV
+    // head j/2, dims 32(j%2) + 8r + mt.  Only lanes whose KV head is head n's
+    // own hold meaningful values.
+    const bool own = (j >> 1) == (n >> 3);
+    const int dbase = 32 * (j & 1);
     const float lsum = head_sum(ts[0].l);
     if (j == 0) {
       sh.sm_m[wave][n] = ts[0].m;
@@ -552,25 +737,68 @@ __device__ __forceinline__ void process_segment(const StepArgs &a, int b, const 
       a.part_ml[e * 2 + 1] = lt;
     }
   } else {
+    // Merge chunk lane 1 into chunk lane 0 (a segment of one chunk leaves lane
+    // 1 empty).  Lane (n, j) of the wave's column tile ct holds column 16ct + n,
+    // dims 16j + 4r + dt in o[dt][c][r].
+    float lsum[2];
 #pragma unroll
-    for (int tk = 0; tk < NT; ++tk) {
-      const float lsum = head_sum(ts[tk].l);
-      if (!ts[tk].live) continue;
-      const int jt = wave + WAVES * tk;
-      const size_t e = ((size_t)slot * a.L + jt) * HQ + n;
-      if (j == 0) {
-        a.part_ml[e * 2] = ts[tk].m;
-        a.part_ml[e * 2 + 1] = lsum;
-      }
-      if (own) {
+    for (int c = 0; c < 2; ++c) lsum[c] = head_sum(vs.l[c]);
+    if (nseg > 1) {   // uniform
+      __syncthreads();   // every wave is done with the Q^T operands (they share the buffer)
+      if (cl == 1) {
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          float *dst = a.part_o + e * D + dbase + 8 * rr;
-          *reinterpret_cast<f32x4 *>(dst) =
-              f32x4{ts[tk].o[0][rr], ts[tk].o[1][rr], ts[tk].o[2][rr], ts[tk].o[3][rr]};
-          *reinterpret_cast<f32x4 *>(dst + 4) =
-              f32x4{ts[tk].o[4][rr], ts[tk].o[5][rr], ts[tk].o[6][rr], ts[tk].o[7][rr]};
+        for (int c = 0; c < 2; ++c) {
+          const int ct = 2 * half + c;
+          if (ct >= nct) break;
+          float *row = sh.mrg[g][16 * ct + n];
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr)
+            *reinterpret_cast<f32x4 *>(row + 16 * j + 4 * rr) =
+                f32x4{vs.o[0][c][rr], vs.o[1][c][rr], vs.o[2][c][rr], vs.o[3][c][rr]};
+          if (j == 0) {
+            sh.mrg_ml[g][16 * ct + n][0] = vs.m[c];
+            sh.mrg_ml[g][16 * ct + n][1] = lsum[c];
+          }
         }
+      }
+      __syncthreads();
+      if (cl == 0) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const int ct = 2 * half + c;
+          if (ct >= nct) break;
+          const float *row = sh.mrg[g][16 * ct + n];
+          const float m1 = sh.mrg_ml[g][16 * ct + n][0], l1 = sh.mrg_ml[g][16 * ct + n][1];
+          const float M = fmaxf(vs.m[c], m1);
+          const float c0 = vs.m[c] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(vs.m[c] - M);
+          const float c1 = m1 == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m1 - M);
+          lsum[c] = lsum[c] * c0 + l1 * c1;
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            const f32x4 v = *reinterpret_cast<const f32x4 *>(row + 16 * j + 4 * rr);
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) vs.o[dt][c][rr] = vs.o[dt][c][rr] * c0 + v[dt] * c1;
+          }
+          vs.m[c] = M;
+        }
+      }
+    }
+    if (cl == 0) {
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const int ct = 2 * half + c;
+        const int tk = 2 * ct + (n >> 3);
+        if (ct >= nct) break;
+        if (tk >= a.L) continue;
+        const size_t e = ((size_t)slot * a.L + tk) * HQ + 8 * g + (n & 7);
+        if (j == 0) {
+          a.part_ml[e * 2] = vs.m[c];
+          a.part_ml[e * 2 + 1] = lsum[c];
+        }
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr)
+          *reinterpret_cast<f32x4 *>(a.part_o + e * D + 16 * j + 4 * rr) =
+              f32x4{vs.o[0][c][rr], vs.o[1][c][rr], vs.o[2][c][rr], vs.o[3][c][rr]};
       }
     }
   }
@@ -585,7 +813,7 @@ __device__ __forceinline__ void process_segment(const StepArgs &a, int b, const 
 // request; segment (w, b) writes its partial to slot w + b (slots are unique
 // because both w and b grow along the chunk space).  The combine kernel then
 // merges each request's slots.
-template <int MODE, int NT, int NBUF>
+template <int MODE, int NBUF>
 __global__ __launch_bounds__(THREADS, 2) void attn_kernel(StepArgs a) {
   __shared__ __attribute__((aligned(16))) Lds sh;
   const int tid = threadIdx.x;
@@ -663,16 +891,16 @@ __global__ __launch_bounds__(THREADS, 2) void attn_kernel(StepArgs a) {
     const int y = (int)(ys < nb ? ys : nb);
     if (y <= x) continue;
     const KeyRange r = range_from(a, sh.req_len[b], sh.req_p0[b]);
-    process_segment<MODE, NT, NBUF>(a, b, r, x, y, w + b, sh);
+    process_segment<MODE, NBUF>(a, b, r, x, y, w + b, sh);
   }
 }
 
 void launch_attn(const StepArgs &a, hipStream_t stream) {
   const dim3 grid(a.work_groups), block(THREADS);
   if (a.L == 1)
-    hipLaunchKernelGGL((attn_kernel<0, 1, MUSEATTN_DECODE_NBUF>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((attn_kernel<0, MUSEATTN_DECODE_NBUF>), grid, block, 0, stream, a);
   else
-    hipLaunchKernelGGL((attn_kernel<1, 1, 2>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((attn_kernel<2, MUSEATTN_VERIFY_NBUF>), grid, block, 0, stream, a);
 }
 
 }  // namespace museattn
