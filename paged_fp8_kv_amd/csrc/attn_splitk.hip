@@ -52,8 +52,11 @@ struct TokState {
   bool live;
 };
 
+// Decode: the B operand of S^T per K-step kk (hi and lo parts), one copy in
+// LDS for the work-group's 8 waves (they all serve the same token): [kk][hi,
+// lo][lane].
 struct QOps {
-  bf16x8 hi[4], lo[4];   // B operand of S^T per K-step
+  bf16x8 op[4][2][64];
 };
 
 __device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t x, uint32_t y) {
@@ -120,8 +123,9 @@ __device__ __forceinline__ void load_rows(RowBuf &rb, const uint8_t *__restrict_
 }
 
 template <int NT>
-__device__ __forceinline__ void compute_chunk(const RowBuf &rb, int u0, int j,
-                                              TokState (&ts)[NT], const QOps (&q)[NT]) {
+__device__ __forceinline__ void compute_chunk(const RowBuf &rb, int u0, int lane,
+                                              TokState (&ts)[NT], const QOps &q) {
+  const int j = lane >> 4;
   // K operands: tile t (keys 16t..16t+15), K-step kk = (KV head kk/2, 8-byte half kk%2)
   bf16x8 ka[2][4];
 #pragma unroll
@@ -148,10 +152,11 @@ __device__ __forceinline__ void compute_chunk(const RowBuf &rb, int u0, int j,
     f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[0][kk], q[tk].hi[kk], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[1][kk], q[tk].hi[kk], s1, 0, 0, 0);
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[0][kk], q[tk].lo[kk], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[1][kk], q[tk].lo[kk], s1, 0, 0, 0);
+      const bf16x8 qh = q.op[kk][0][lane], ql = q.op[kk][1][lane];
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[0][kk], qh, s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[1][kk], qh, s1, 0, 0, 0);
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[0][kk], ql, s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[1][kk], ql, s1, 0, 0, 0);
     }
     float sc[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
     // only a chunk that straddles the token's visible range needs a mask
@@ -404,12 +409,17 @@ __device__ __forceinline__ void pack_q(const float (&y)[16], int half, float mul
 // kk/2, so it holds head n's values when n/8 == kk/2 and zeros otherwise; q is
 // multiplied by log2(e)/8 and kv_scale (qmul).
 __device__ __forceinline__ void make_q(const StepArgs &a, const QIn &in, const f32x4 (&wv)[4],
-                                       int j, int n, float qmul, const float2 *cs, QOps &qo) {
+                                       int lane, float qmul, const float2 *cs, QOps &qo) {
+  const int n = lane & 15, j = lane >> 4;
   float y[16];
   q_values(a, in, wv, j, cs, y);
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk)
-    pack_q(y, kk & 1, (n >> 3) == (kk >> 1) ? qmul : 0.0f, qo.hi[kk], qo.lo[kk]);
+  for (int kk = 0; kk < 4; ++kk) {
+    bf16x8 hi, lo;
+    pack_q(y, kk & 1, (n >> 3) == (kk >> 1) ? qmul : 0.0f, hi, lo);
+    qo.op[kk][0][lane] = hi;
+    qo.op[kk][1][lane] = lo;
+  }
 }
 
 // The new k and v rows of the block tokens flagged in `own` (bit jt = token
@@ -519,6 +529,7 @@ struct Lds {
     VerifyQ vq[2];              // verify chunk loop: Q^T operands per KV head
   };
   float mrg_ml[2][64][2];       // verify merge: its (max, sum) per column
+  QOps dq;                      // decode: the token's Q^T operands
   float sm_m[WAVES][HQ];
   float sm_l[WAVES][HQ];
   int pref[MAX_BATCH + 1];
@@ -584,7 +595,6 @@ __device__ __forceinline__ void process_segment(const StepArgs &a, int b, const 
     lo = a.sliding ? p - (WINDOW - 1) : 0;
   };
   TokState ts[1];
-  QOps qo[1];
   VerifyState vs;
   if constexpr (MODE == 0) {
     token_range(true, pos[0], ts[0].lo, ts[0].hi);
@@ -593,7 +603,7 @@ __device__ __forceinline__ void process_segment(const StepArgs &a, int b, const 
     ts[0].l = 0.0f;
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt) ts[0].o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    make_q(a, qin, wv, j, n, qmul, sh.cs[0], qo[0]);
+    if (wave == 0) make_q(a, qin, wv, lane, qmul, sh.cs[0], sh.dq);   // published by the barrier below
   } else {
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
@@ -664,14 +674,14 @@ __device__ __forceinline__ void process_segment(const StepArgs &a, int b, const 
         for (; i + NBUF <= nloc; i += NBUF) {
 #pragma unroll
           for (int k = 0; k < NBUF; ++k) {
-            compute_chunk<1>(buf[k], key_of(i + k), j, ts, qo);
+            compute_chunk<1>(buf[k], key_of(i + k), lane, ts, sh.dq);
             const int inext = i + k + NBUF;
             load_rows(buf[k], a.k_cache, a.v_cache, rows_of(inext < last ? inext : last), n, j);
           }
         }
 #pragma unroll
         for (int k = 0; k < NBUF - 1; ++k)
-          if (i + k < nloc) compute_chunk<1>(buf[k], key_of(i + k), j, ts, qo);
+          if (i + k < nloc) compute_chunk<1>(buf[k], key_of(i + k), lane, ts, sh.dq);
       } else {
         RowBuf2 buf[NBUF];
 #pragma unroll
