@@ -139,8 +139,9 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the "
-              "multi-GPU sharding of the step is described in DESIGN.md, not run.",
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the step "
+              "shards by request or by key range without kernel changes, but no multi-GPU "
+              "run is implemented here.",
               file=sys.stderr)
         sys.exit(2)
 

@@ -18,7 +18,7 @@ program (numpy matmul and exp are the only library steps):
                                                2048 positions p-2047..p (sliding)
     out = rmsnorm(a) * sigmoid(gate)           per head, bf16 [B, L, 16*64]
 
-Readings where the page is silent (each is also listed in the design doc):
+Readings where the page is silent:
   * qkv row layout [q 16x64 | k 2x64 | v 2x64 | gate 16x64], head-major.
   * query head h reads KV head h // 8 (contiguous GQA groups of 8).
   * every rmsnorm carries a per-dimension weight of 64 values, used as given

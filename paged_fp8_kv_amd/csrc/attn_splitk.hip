@@ -335,12 +335,17 @@ __device__ __forceinline__ uint8_t to_e4m3(float x) {
 }
 
 // RoPE factors of one block token: pair i (dims i, i+32) turns by
-// theta = fp32(p) * inv_i with inv_i = base^(-i/32) rounded to fp32; sin/cos
-// of that fp32 angle are taken in double so large positions keep full
-// accuracy (task page "Gated attention decode", section "What to compute",
-// the rope line; sliding layers only, section "Shapes").
-__device__ __forceinline__ float2 rope_cs(float rope_base, int p, int i) {
-  const float inv = (float)pow((double)rope_base, -(double)i / 32.0);
+// theta = fp32(p) * inv_i with inv_i = base^(-i/32) rounded to fp32 (a table
+// the host fills once per call); sin/cos of that fp32 angle are taken in
+// double so large positions keep full accuracy (task page "Gated attention
+// decode", section "What to compute", the rope line; sliding layers only,
+// section "Shapes").  The table is read from the kernel's argument block,
+// whose first member is the StepArgs (a per-lane index into the by-value
+// argument itself would make the compiler copy it to scratch).
+__device__ __forceinline__ float2 rope_cs(int p, int i) {
+  const char *args = (const char *)__builtin_amdgcn_kernarg_segment_ptr();
+  const float *rope_inv = reinterpret_cast<const float *>(args + offsetof(StepArgs, rope_inv));
+  const float inv = rope_inv[i];
   const float th = (float)p * inv;
   double sd, cd;
   sincos((double)th, &sd, &cd);
@@ -533,7 +538,7 @@ struct Lds {
   float sm_m[WAVES][HQ];
   float sm_l[WAVES][HQ];
   int pref[MAX_BATCH + 1];
-  int scan[THREADS];
+  int scan[WAVES];            // the plan's per-wave totals
   int req_len[MAX_BATCH];    // seq_lens[b], kept from the plan
   int req_p0[MAX_BATCH];     // positions[b * L] (sliding layers)
 };
@@ -583,7 +588,7 @@ __device__ __forceinline__ void process_segment(const StepArgs &a, int b, const 
 
   __syncthreads();   // the previous segment is done with sh.cs, sh.lrows and the merge buffers
   if (a.sliding) {
-    if (tid < a.L * 32) sh.cs[tid >> 5][tid & 31] = rope_cs(a.rope_base, a.positions[b * a.L + (tid >> 5)], tid & 31);
+    if (tid < a.L * 32) sh.cs[tid >> 5][tid & 31] = rope_cs(a.positions[b * a.L + (tid >> 5)], tid & 31);
     __syncthreads();
   }
   store_table(a, tin, sh.lrows);
@@ -850,23 +855,32 @@ __global__ __launch_bounds__(THREADS, 2) void attn_kernel(StepArgs a) {
       sh.req_p0[RPT * tid + k] = p0[k];
     }
   }
-  sh.scan[tid] = sum;
-  __syncthreads();
-  for (int off = 1; off < THREADS; off <<= 1) {
-    const int v = tid >= off ? sh.scan[tid - off] : 0;
-    __syncthreads();
-    sh.scan[tid] += v;
-    __syncthreads();
-  }
   {
-    int run = sh.scan[tid] - sum;
+    // exclusive prefix sum over the threads: a shuffle scan inside each wave,
+    // then the 8 wave totals through LDS
+    const int lane = tid & 63, wave = tid >> 6;
+    int incl = sum;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int v = __shfl_up(incl, off);
+      incl += lane >= off ? v : 0;
+    }
+    if (lane == 63) sh.scan[wave] = incl;
+    __syncthreads();
+    int run = incl - sum, total = 0;
+#pragma unroll
+    for (int w2 = 0; w2 < WAVES; ++w2) {
+      const int t = sh.scan[w2];
+      run += w2 < wave ? t : 0;
+      total += t;
+    }
 #pragma unroll
     for (int k = 0; k < RPT; ++k) {
       const int b = RPT * tid + k;
       if (b < a.B) sh.pref[b] = run;
       run += cnt[k];
     }
-    if (tid == THREADS - 1) sh.pref[a.B] = sh.scan[THREADS - 1];
+    if (tid == 0) sh.pref[a.B] = total;
   }
   __syncthreads();
   // Cost space: request b occupies seg_cost units (its segment start-up, in

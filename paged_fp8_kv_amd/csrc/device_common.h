@@ -39,7 +39,8 @@ struct StepArgs {
   float *part_ml;          // [slot][L][16][2] (reference max in log2 units, sum)
   float *part_o;           // [slot][L][16][64] unnormalised partial outputs
   int64_t num_rows;
-  float kv_scale, eps, q_scale, rope_base;
+  float kv_scale, eps, q_scale;
+  float rope_inv[32];      // RoPE inverse frequencies fp32(rope_base^(-i/32)), pair i
   int B, L, table_stride, max_seq_len, page_size, sliding;
   int work_groups;         // attention work-groups launched (each takes an equal
                            // share of all requests' key chunks)

@@ -155,7 +155,10 @@ int museattn_attn_step_profiled(const void *qkv, const int32_t *positions, const
   a.kv_scale = kv_scale;
   a.eps = params->eps;
   a.q_scale = params->q_scale;
-  a.rope_base = params->rope_base;
+  // RoPE inverse frequencies, one per pair: constants of the rotation (they
+  // depend on rope_base only), rounded to fp32 as the angle product uses them
+  for (int i = 0; i < 32; ++i)
+    a.rope_inv[i] = (float)std::pow((double)params->rope_base, -(double)i / 32.0);
   a.B = B;
   a.L = L;
   a.table_stride = table_stride;
