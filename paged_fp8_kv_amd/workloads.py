@@ -11,7 +11,19 @@ Shapes follow the task page "Gated attention decode (muse_attention_decode)",
 section "Shapes": 16 query heads and 2 KV heads of dim 64 per GPU, decode
 (L = 1) or an 8-token verify block, contexts around 80K, page size 1 or 64,
 kv_scale 1 or 1/64.  The page's "spread" and "dist" input families are not
-defined beyond a sentence each; the draws below stand in for them.
+defined beyond a sentence each; the draws below stand in for them:
+  soft       cached K and V elements are clipped N(0,1) draws;
+  coherent   (section "Correctness": each head's keys share a direction, so
+             attention spreads over many keys; on full layers the values of the
+             low-attention keys share a direction too) -- per request and KV
+             head, keys are 8 d + 0.1 z and, on full layers, values are
+             8 w + 0.5 z, for unit vectors d, w and z ~ N(0,1) per element;
+  edges      (section "Correctness": keys at the window's edges) -- soft draws,
+             with the keys and values at the edges of the visible range
+             enlarged 6-fold (clipped): on sliding layers the first visible
+             position of each block token's window and the one just outside
+             it, on full layers positions 0 and 1; on both, the last two cached
+             positions.
 """
 from __future__ import annotations
 
@@ -46,6 +58,7 @@ class Workload:
     table: np.ndarray        # int32 [B, table_stride]; unused slots = -1
     pages: list = field(default_factory=list)  # per request: int64 page (or row) ids in order
     origin: list = field(default_factory=list)  # request ids in the workload drawn (subsets)
+    dist: str = "soft"       # "soft", "coherent" or "edges" (module docstring)
 
     @property
     def T(self) -> int:
@@ -86,7 +99,7 @@ class Workload:
                        qkv=self.qkv.view(self.B, self.L, QKV_WIDTH)[req].reshape(-1, QKV_WIDTH).clone(),
                        w_q=self.w_q, w_k=self.w_k, w_o=self.w_o, table=self.table[req].copy(),
                        pages=[self.pages[b] for b in req],
-                       origin=[self.origin[b] if self.origin else b for b in req])
+                       origin=[self.origin[b] if self.origin else b for b in req], dist=self.dist)
         return sub
 
     def cache_values(self, b: int) -> tuple[np.ndarray, np.ndarray]:
@@ -95,6 +108,28 @@ class Workload:
         src = self.origin[b] if self.origin else b
         rng = np.random.Generator(np.random.PCG64([self.seed, src]))
         x = rng.standard_normal(2 * n * ROW_BYTES, dtype=np.float32)
+        if self.dist == "coherent":
+            x = x.reshape(2, n, HKV, D)
+            rd = np.random.Generator(np.random.PCG64([self.seed, src, 1]))
+            dirs = rd.standard_normal((2, HKV, D))
+            dirs /= np.linalg.norm(dirs, axis=-1, keepdims=True)
+            x[0] = 8.0 * dirs[0][None] + 0.1 * x[0]
+            if self.layer_kind == FULL:
+                x[1] = 8.0 * dirs[1][None] + 0.5 * x[1]
+            x = x.reshape(-1).astype(np.float32)
+        elif self.dist == "edges":
+            x = x.reshape(2, n, HKV, D)
+            first = int(self.ctx[b])          # position of block token 0
+            if self.layer_kind == SLIDING:
+                edge = [first - 2048 + j for j in range(self.L + 1)]
+            else:
+                edge = [0, 1]
+            edge += [n - 2, n - 1]
+            for u in sorted({u for u in edge if 0 <= u < n}):
+                x[:, u] *= 6.0
+            x = x.reshape(-1)
+        elif self.dist != "soft":
+            raise ValueError(f"unknown distribution {self.dist!r}")
         np.clip(x, -_CLIP, _CLIP, out=x)
         xt = torch.from_numpy(x)
         if self.kv_scale != 1.0:
@@ -108,8 +143,9 @@ def _stream(seed: int, tag: int) -> np.random.Generator:
 
 
 def make(name: str, seed: int, B: int, L: int, ctx, layer_kind: int, page_size: int,
-         kv_scale: float, pool_rows: int | None = None) -> Workload:
-    """Draw one workload.  ctx: int, or (lo, hi) for a uniform draw per request."""
+         kv_scale: float, pool_rows: int | None = None, dist: str = "soft") -> Workload:
+    """Draw one workload.  ctx: int, or (lo, hi) for a uniform draw per request;
+    dist: the cached K/V distribution (module docstring)."""
     if isinstance(ctx, tuple):
         ctx_arr = _stream(seed, 3).integers(ctx[0], ctx[1] + 1, size=B).astype(np.int64)
     else:
@@ -146,7 +182,7 @@ def make(name: str, seed: int, B: int, L: int, ctx, layer_kind: int, page_size: 
     return Workload(name=name, seed=seed, B=B, L=L, layer_kind=layer_kind, page_size=ps,
                     kv_scale=float(np.float32(kv_scale)), ctx=ctx_arr,
                     num_rows=pool_units * ps, qkv=qkv, w_q=w[0], w_k=w[1], w_o=w[2],
-                    table=table, pages=pages)
+                    table=table, pages=pages, dist=dist)
 
 
 # The five workloads of record (seed = 1000 + id); config 3 runs both layer kinds.

@@ -103,6 +103,37 @@ def test_edge_parity(case):
     _untouched_rows_kept(w, d, host)
 
 
+# The page's gate tests that the edge cases above do not already cover
+# (section "Correctness" gives the distributions; "heads dp" shapes run at this
+# shard's head count; "spread mixed" draws each context from [ctx/2, ctx]).
+GATE = [
+    # name, B, L, ctx, kind, page_size, kv_scale, dist
+    ("gate-b8-full-ctx8192-spread", 8, 1, (4096, 8192), W.FULL, 1, 1.0, "soft"),
+    ("gate-b2-L8-full-ctx100000-p1", 2, 8, 100000, W.FULL, 1, 1.0, "soft"),
+    ("gate-b4-sliding-ctx6000-edges-p1", 4, 1, 6000, W.SLIDING, 1, 1.0, "edges"),
+    ("gate-b4-L8-full-ctx6000-edges", 4, 8, 6000, W.FULL, 64, 1.0, "edges"),
+    ("gate-b4-full-ctx80000-spread-soft", 4, 1, (40000, 80000), W.FULL, 64, 1.0, "soft"),
+    ("gate-b4-L8-sliding-ctx6000-soft-p1", 4, 8, 6000, W.SLIDING, 1, 1.0, "soft"),
+    ("gate-b4-full-ctx80000-spread-coherent-p1", 4, 1, (40000, 80000), W.FULL, 1, 1.0, "coherent"),
+    ("gate-b2-L8-full-ctx20000-coherent", 2, 8, 20000, W.FULL, 64, 1.0, "coherent"),
+    ("b3-L8-sliding-ctx5000-coherent", 3, 8, 5000, W.SLIDING, 1, 1.0, "coherent"),
+    ("b2-L3-sliding-ctx3000-edges-kv1/64", 2, 3, 3000, W.SLIDING, 64, 1.0 / 64, "edges"),
+]
+
+
+@pytest.mark.parametrize("case", GATE, ids=[c[0] for c in GATE])
+def test_gate_parity(case):
+    name, B, L, ctx, kind, ps, kv, dist = case
+    w = W.make(name, 88, B, L, ctx, kind, ps, kv, dist=dist)
+    log(f"[gate] {name} ctx={w.ctx.tolist()[:4]} dist={dist}")
+    host = W.build_pools_numpy(w)
+    d = upload(w)
+    run(w, d)
+    torch.cuda.synchronize()
+    full_check(w, d, host_pools=host)
+    _untouched_rows_kept(w, d, host)
+
+
 @pytest.mark.slow
 def test_million_key_verify_block():
     """A full layer over 1,048,576 cached keys with an 8-token block."""
