@@ -49,7 +49,6 @@ struct TokState {
   float m;      // running max (log2 units), same in the 4 lanes of a head
   float l;      // this lane's share of the running sum
   int lo, hi;   // visible key positions of the token, inclusive
-  bool live;
 };
 
 // Decode: the B operand of S^T per K-step kk (hi and lo parts), one copy in
@@ -122,9 +121,8 @@ __device__ __forceinline__ void load_rows(RowBuf &rb, const uint8_t *__restrict_
     rb.v[i] = *reinterpret_cast<const uint2 *>(vc + (uint64_t)vr[i] * ROW + 8 * n);
 }
 
-template <int NT>
-__device__ __forceinline__ void compute_chunk(const RowBuf &rb, int u0, int lane,
-                                              TokState (&ts)[NT], const QOps &q) {
+__device__ __forceinline__ void compute_chunk(const RowBuf &rb, int u0, int lane, TokState &st,
+                                              const QOps &q) {
   const int j = lane >> 4;
   // K operands: tile t (keys 16t..16t+15), K-step kk = (KV head kk/2, 8-byte half kk%2)
   bf16x8 ka[2][4];
@@ -145,63 +143,58 @@ __device__ __forceinline__ void compute_chunk(const RowBuf &rb, int u0, int lane
 #pragma unroll
   for (int mt = 0; mt < 8; ++mt) vb[mt] = fp8x8_to_bf16(tx[mt], ty[mt]);
 
+  f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int tk = 0; tk < NT; ++tk) {
-    TokState &st = ts[tk];
-    if (!st.live) continue;
-    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const bf16x8 qh = q.op[kk][0][lane], ql = q.op[kk][1][lane];
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[0][kk], qh, s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[1][kk], qh, s1, 0, 0, 0);
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[0][kk], ql, s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[1][kk], ql, s1, 0, 0, 0);
-    }
-    float sc[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
-    // only a chunk that straddles the token's visible range needs a mask
-    if (u0 < st.lo || u0 + CHUNK - 1 > st.hi) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int u = u0 + (i >> 2) * 16 + 4 * j + (i & 3);
-        if (u < st.lo || u > st.hi) sc[i] = -INFINITY;
-      }
-    }
-    float cmax = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
-                       fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
-    cmax = head_max(cmax);
-    // Lazy rescale: the reference max st.m only moves when some head's chunk
-    // max exceeds it by more than RESCALE_SLACK (log2 units), so P <= 2^SLACK.
-    // Any reference gives the same softmax; this one skips most rescales.
-    if (__any(cmax > st.m + RESCALE_SLACK)) {
-      const float mnew = fmaxf(st.m, cmax);
-      const float alpha = mnew == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(st.m - mnew);
-      st.l *= alpha;
-#pragma unroll
-      for (int mt = 0; mt < 8; ++mt) st.o[mt] *= alpha;
-      st.m = mnew;
-    }
-    const float muse = st.m == -INFINITY ? 0.0f : st.m;
-    float pv[8];
+  for (int kk = 0; kk < 4; ++kk) {
+    const bf16x8 qh = q.op[kk][0][lane], ql = q.op[kk][1][lane];
+    s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[0][kk], qh, s0, 0, 0, 0);
+    s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[1][kk], qh, s1, 0, 0, 0);
+    s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[0][kk], ql, s0, 0, 0, 0);
+    s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[1][kk], ql, s1, 0, 0, 0);
+  }
+  float sc[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+  // only a chunk that straddles the token's visible range needs a mask
+  if (u0 < st.lo || u0 + CHUNK - 1 > st.hi) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      pv[i] = __builtin_amdgcn_exp2f(sc[i] - muse);
-      st.l += pv[i];
+      const int u = u0 + (i >> 2) * 16 + 4 * j + (i & 3);
+      if (u < st.lo || u > st.hi) sc[i] = -INFINITY;
     }
-    bf16x8 ph, pl;
+  }
+  float cmax = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
+                     fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
+  cmax = head_max(cmax);
+  // Lazy rescale: the reference max st.m only moves when some head's chunk
+  // max exceeds it by more than RESCALE_SLACK (log2 units), so P <= 2^SLACK.
+  // Any reference gives the same softmax; this one skips most rescales.
+  if (__any(cmax > st.m + RESCALE_SLACK)) {
+    const float mnew = fmaxf(st.m, cmax);
+    const float alpha = mnew == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(st.m - mnew);
+    st.l *= alpha;
 #pragma unroll
-    for (int i = 0; i < 8; i += 2) {
-      const f32x2 f = {pv[i], pv[i + 1]};
-      const bf16x2 h = __builtin_convertvector(f, bf16x2);
-      const bf16x2 r = __builtin_convertvector(f - __builtin_convertvector(h, f32x2), bf16x2);
-      ph[i] = h[0]; ph[i + 1] = h[1];
-      pl[i] = r[0]; pl[i + 1] = r[1];
-    }
+    for (int mt = 0; mt < 8; ++mt) st.o[mt] *= alpha;
+    st.m = mnew;
+  }
+  const float muse = st.m == -INFINITY ? 0.0f : st.m;
+  float pv[8];
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt) {
-      st.o[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vb[mt], ph, st.o[mt], 0, 0, 0);
-      st.o[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vb[mt], pl, st.o[mt], 0, 0, 0);
-    }
+  for (int i = 0; i < 8; ++i) {
+    pv[i] = __builtin_amdgcn_exp2f(sc[i] - muse);
+    st.l += pv[i];
+  }
+  bf16x8 ph, pl;
+#pragma unroll
+  for (int i = 0; i < 8; i += 2) {
+    const f32x2 f = {pv[i], pv[i + 1]};
+    const bf16x2 h = __builtin_convertvector(f, bf16x2);
+    const bf16x2 r = __builtin_convertvector(f - __builtin_convertvector(h, f32x2), bf16x2);
+    ph[i] = h[0]; ph[i + 1] = h[1];
+    pl[i] = r[0]; pl[i + 1] = r[1];
+  }
+#pragma unroll
+  for (int mt = 0; mt < 8; ++mt) {
+    st.o[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vb[mt], ph, st.o[mt], 0, 0, 0);
+    st.o[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vb[mt], pl, st.o[mt], 0, 0, 0);
   }
 }
 
@@ -599,15 +592,14 @@ __device__ __forceinline__ void process_segment(const StepArgs &a, int b, const 
     hi = live ? (p < r.khi ? p : r.khi) : -1;
     lo = a.sliding ? p - (WINDOW - 1) : 0;
   };
-  TokState ts[1];
+  TokState ts;
   VerifyState vs;
   if constexpr (MODE == 0) {
-    token_range(true, pos[0], ts[0].lo, ts[0].hi);
-    ts[0].live = true;
-    ts[0].m = -INFINITY;
-    ts[0].l = 0.0f;
+    token_range(true, pos[0], ts.lo, ts.hi);
+    ts.m = -INFINITY;
+    ts.l = 0.0f;
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt) ts[0].o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int mt = 0; mt < 8; ++mt) ts.o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
     if (wave == 0) make_q(a, qin, wv, lane, qmul, sh.cs[0], sh.dq);   // published by the barrier below
   } else {
 #pragma unroll
@@ -679,14 +671,14 @@ __device__ __forceinline__ void process_segment(const StepArgs &a, int b, const 
         for (; i + NBUF <= nloc; i += NBUF) {
 #pragma unroll
           for (int k = 0; k < NBUF; ++k) {
-            compute_chunk<1>(buf[k], key_of(i + k), lane, ts, sh.dq);
+            compute_chunk(buf[k], key_of(i + k), lane, ts, sh.dq);
             const int inext = i + k + NBUF;
             load_rows(buf[k], a.k_cache, a.v_cache, rows_of(inext < last ? inext : last), n, j);
           }
         }
 #pragma unroll
         for (int k = 0; k < NBUF - 1; ++k)
-          if (i + k < nloc) compute_chunk<1>(buf[k], key_of(i + k), lane, ts, sh.dq);
+          if (i + k < nloc) compute_chunk(buf[k], key_of(i + k), lane, ts, sh.dq);
       } else {
         RowBuf2 buf[NBUF];
 #pragma unroll
@@ -714,9 +706,9 @@ __device__ __forceinline__ void process_segment(const StepArgs &a, int b, const 
     // own hold meaningful values.
     const bool own = (j >> 1) == (n >> 3);
     const int dbase = 32 * (j & 1);
-    const float lsum = head_sum(ts[0].l);
+    const float lsum = head_sum(ts.l);
     if (j == 0) {
-      sh.sm_m[wave][n] = ts[0].m;
+      sh.sm_m[wave][n] = ts.m;
       sh.sm_l[wave][n] = lsum;
     }
     if (own) {
@@ -724,9 +716,9 @@ __device__ __forceinline__ void process_segment(const StepArgs &a, int b, const 
       for (int rr = 0; rr < 4; ++rr) {
         float *dst = &sh.sm_o[wave][n][dbase + 8 * rr];
         *reinterpret_cast<f32x4 *>(dst) =
-            f32x4{ts[0].o[0][rr], ts[0].o[1][rr], ts[0].o[2][rr], ts[0].o[3][rr]};
+            f32x4{ts.o[0][rr], ts.o[1][rr], ts.o[2][rr], ts.o[3][rr]};
         *reinterpret_cast<f32x4 *>(dst + 4) =
-            f32x4{ts[0].o[4][rr], ts[0].o[5][rr], ts[0].o[6][rr], ts[0].o[7][rr]};
+            f32x4{ts.o[4][rr], ts.o[5][rr], ts.o[6][rr], ts.o[7][rr]};
       }
     }
     __syncthreads();
