@@ -5,7 +5,9 @@
  * The operation is the one defined on the task page "Gated attention decode
  * (muse_attention_decode)", section "What to compute": for every request b
  * and block token j (position p = positions[b*L + j]) of one decode step
- * (L = 1) or one causal verify block (L <= 8):
+ * (L = 1), one causal verify block (L <= 8) or one causal prefill block (up to
+ * 16384 tokens; the attention part of the prefill task page "Prefill layer",
+ * section "Shapes", over the same cache):
  *
  *   q, k, v, gate = split(qkv row)              (section "What to compute")
  *   q = rmsnorm(q) * w_q * q_scale ; k = rmsnorm(k) * w_k
@@ -75,7 +77,8 @@ enum museattn_status {
   MUSEATTN_ERR_NULL = -1,         /* a required pointer is null */
   MUSEATTN_ERR_PAGE_SIZE = -2,    /* page_size is not 1 or 64 */
   MUSEATTN_ERR_LAYER_KIND = -3,   /* layer_kind is not FULL or SLIDING */
-  MUSEATTN_ERR_SHAPE = -4,        /* B (1..1024), L (1..8), max_seq_len or
+  MUSEATTN_ERR_SHAPE = -4,        /* B (1..1024), L (1..16384), B * ceil(L / 16)
+                                     (L > 8) above 4096, max_seq_len or
                                      num_rows out of range */
   MUSEATTN_ERR_TABLE = -5,        /* table_stride < ceil(max_seq_len / page_size) */
   MUSEATTN_ERR_ALIGN = -6,        /* k_cache/v_cache not 16-byte aligned, or
@@ -131,7 +134,10 @@ int museattn_check_args(const void *qkv, const int32_t *positions, const int32_t
  *   layer_kind MUSEATTN_FULL or MUSEATTN_SLIDING
  *   out        bf16 [B][L][1024]
  *   stream     hipStream_t the work is enqueued on (NULL = default stream)
- *   1 <= B <= 1024, 1 <= L <= 8, table_stride >= ceil(max_seq_len / page_size),
+ *   1 <= B <= 1024, 1 <= L <= 16384 with B * ceil(L / 16) <= 4096 when L > 8
+ *   (up to 8 block tokens the new rows are written inside the attention
+ *   kernel; beyond, a first kernel writes them all),
+ *   table_stride >= ceil(max_seq_len / page_size),
  *   L <= max_seq_len <= 2^30, num_rows a multiple of page_size,
  *   workspace  device scratch of >= museattn_workspace_bytes(...) bytes,
  *              256-byte aligned. */

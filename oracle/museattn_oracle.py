@@ -196,12 +196,13 @@ def visible_keys(p: int, window: int | None) -> tuple[int, int]:
     return lo, p
 
 
-def attend(q, k_pool, v_pool, table, positions, B, L, page_size, kv_scale, window):
+def attend(q, k_pool, v_pool, table, positions, B, L, page_size, kv_scale, window, tokens=None):
     """a = softmax(q . K^T / 8) . V per (token, head), two passes, float64.
 
     K and V are read through the table from the pools (anything indexable by an
     int64 row array giving [n, 2, 64] bytes) and dequantised as decode*kv_scale.
     window=None attends to every key 0..p, else to the last `window` positions.
+    tokens: block-token indices j to compute (None = all); the others stay 0.
     Returns a float64 [B*L, 16, 64]."""
     q = np.asarray(q, dtype=np.float64)
     ks = float(kv_scale)
@@ -214,7 +215,7 @@ def attend(q, k_pool, v_pool, table, positions, B, L, page_size, kv_scale, windo
         rows = cache_row(table, b, np.arange(ulo, uhi + 1), page_size)
         kd = _DECODE_TABLE[k_pool[rows]] * ks          # [n, 2, 64]
         vd = _DECODE_TABLE[v_pool[rows]] * ks
-        for j in range(L):
+        for j in (range(L) if tokens is None else tokens):
             t = b * L + j
             lo, hi = spans[j]
             kj, vj = kd[lo - ulo:hi - ulo + 1], vd[lo - ulo:hi - ulo + 1]
@@ -234,12 +235,14 @@ def gated_output(a, gate, w_o, eps):
 
 def attn_step(qkv, positions, table, k_pool, v_pool, *, B, L, page_size, layer_kind,
               kv_scale, w_q, w_k, w_o, eps, q_scale, rope_base=10000.0, window=WINDOW,
-              new_rows=None):
+              new_rows=None, tokens=None):
     """The whole step.  Writes the new rows into k_pool / v_pool (in place).
 
     new_rows: optional (kbyte, vbyte) to write instead of the oracle's own
     quantised k, v -- used to attend to another implementation's written
     entries, as the page's correctness section does for the cache check.
+    tokens: block-token indices whose outputs are computed (None = all; the
+    others are left 0) -- the new rows of every token are written regardless.
     Returns (out float64 [B, L, 16*64], kbyte, vbyte)."""
     sliding = layer_kind == SLIDING
     q, kbyte, vbyte, gate = prologue(qkv, positions, w_q, w_k, eps=eps, q_scale=q_scale,
@@ -247,6 +250,6 @@ def attn_step(qkv, positions, table, k_pool, v_pool, *, B, L, page_size, layer_k
     wk, wv = (kbyte, vbyte) if new_rows is None else new_rows
     write_rows(k_pool, v_pool, table, positions, B, L, page_size, wk, wv)
     a = attend(q, k_pool, v_pool, table, positions, B, L, page_size, kv_scale,
-               window if sliding else None)
+               window if sliding else None, tokens)
     out = gated_output(a, gate, w_o, eps)
     return out.reshape(B, L, HQ * D), kbyte, vbyte

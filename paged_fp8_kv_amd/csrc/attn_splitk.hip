@@ -244,105 +244,105 @@ __device__ __forceinline__ void load_rows2(RowBuf2 &rb, const uint8_t *__restric
     rb.v[i] = *reinterpret_cast<const uint32_t *>(vc + (uint64_t)vr[i] * ROW + 64 * g + 4 * n);
 }
 
-__device__ __forceinline__ void compute_chunk2(const RowBuf2 &rb, int u0, int lane, int half,
-                                               int nct, VerifyState &st, const VerifyQ &q) {
-  const int j = lane >> 4;
-  bf16x8 ka[2][2];
+// The chunk's K_g and V_g^T operands (fp8 -> bf16 is exact).
+struct ChunkOps2 {
+  bf16x8 ka[2][2];   // [key tile][K-step]
+  bf16x8 va[4];      // [dim tile]
+};
+
+__device__ __forceinline__ ChunkOps2 chunk_ops2(const RowBuf2 &rb) {
+  ChunkOps2 op;
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
-    ka[t][0] = fp8x8_to_bf16(rb.k[t].x, rb.k[t].y);
-    ka[t][1] = fp8x8_to_bf16(rb.k[t].z, rb.k[t].w);
+    op.ka[t][0] = fp8x8_to_bf16(rb.k[t].x, rb.k[t].y);
+    op.ka[t][1] = fp8x8_to_bf16(rb.k[t].z, rb.k[t].w);
   }
   uint32_t ty[4], tz[4];
   transpose4x4(rb.v[0], rb.v[1], rb.v[2], rb.v[3], ty[0], ty[1], ty[2], ty[3]);
   transpose4x4(rb.v[4], rb.v[5], rb.v[6], rb.v[7], tz[0], tz[1], tz[2], tz[3]);
-  bf16x8 va[4];
 #pragma unroll
-  for (int dt = 0; dt < 4; ++dt) va[dt] = fp8x8_to_bf16(ty[dt], tz[dt]);
+  for (int dt = 0; dt < 4; ++dt) op.va[dt] = fp8x8_to_bf16(ty[dt], tz[dt]);
+  return op;
+}
 
+// One column tile of one chunk: S^T (32 keys x 16 columns) from the tile's
+// Q^T operands (K-steps 0, 1; hi and lo), mask, online softmax of the
+// columns, and O^T += V^T . P^T into state slot c.
+__device__ __forceinline__ void tile_step(const ChunkOps2 &op, bf16x8 qh0, bf16x8 ql0, bf16x8 qh1,
+                                          bf16x8 ql1, int u0, int j, VerifyState &st, int c) {
+  f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+  s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op.ka[0][0], qh0, s0, 0, 0, 0);
+  s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op.ka[1][0], qh0, s1, 0, 0, 0);
+  s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op.ka[0][0], ql0, s0, 0, 0, 0);
+  s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op.ka[1][0], ql0, s1, 0, 0, 0);
+  s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op.ka[0][1], qh1, s0, 0, 0, 0);
+  s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op.ka[1][1], qh1, s1, 0, 0, 0);
+  s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op.ka[0][1], ql1, s0, 0, 0, 0);
+  s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op.ka[1][1], ql1, s1, 0, 0, 0);
+  float sc[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+  const int lo = st.lo[c], hi = st.hi[c];
+  if (u0 < lo || u0 + CHUNK - 1 > hi) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int u = u0 + (i >> 2) * 16 + 4 * j + (i & 3);
+      if (u < lo || u > hi) sc[i] = -INFINITY;
+    }
+  }
+  float cmax = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
+                     fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
+  cmax = head_max(cmax);
+  if (__any(cmax > st.m[c] + RESCALE_SLACK)) {
+    const float mnew = fmaxf(st.m[c], cmax);
+    const float alpha = mnew == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(st.m[c] - mnew);
+    st.l[c] *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) st.o[dt][c] *= alpha;
+    st.m[c] = mnew;
+  }
+  const float muse = st.m[c] == -INFINITY ? 0.0f : st.m[c];
+  float pv[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    pv[i] = __builtin_amdgcn_exp2f(sc[i] - muse);
+    st.l[c] += pv[i];
+  }
+  bf16x8 ph, pl;
+#pragma unroll
+  for (int i = 0; i < 8; i += 2) {
+    const f32x2 f = {pv[i], pv[i + 1]};
+    const bf16x2 h = __builtin_convertvector(f, bf16x2);
+    const bf16x2 r = __builtin_convertvector(f - __builtin_convertvector(h, f32x2), bf16x2);
+    ph[i] = h[0]; ph[i + 1] = h[1];
+    pl[i] = r[0]; pl[i + 1] = r[1];
+  }
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) {
+    st.o[dt][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op.va[dt], ph, st.o[dt][c], 0, 0, 0);
+    st.o[dt][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op.va[dt], pl, st.o[dt][c], 0, 0, 0);
+  }
+}
+
+// Verify: the wave's two column tiles (2 half, 2 half + 1), Q^T from LDS.
+__device__ __forceinline__ void compute_chunk2(const RowBuf2 &rb, int u0, int lane, int half,
+                                               int nct, VerifyState &st, const VerifyQ &q) {
+  const ChunkOps2 op = chunk_ops2(rb);
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
     const int ct = 2 * half + c;
     if (ct >= nct) break;   // uniform
-    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const bf16x8 qh = q.op[ct][kk][0][lane], ql = q.op[ct][kk][1][lane];
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[0][kk], qh, s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[1][kk], qh, s1, 0, 0, 0);
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[0][kk], ql, s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[1][kk], ql, s1, 0, 0, 0);
-    }
-    float sc[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
-    const int lo = st.lo[c], hi = st.hi[c];
-    if (u0 < lo || u0 + CHUNK - 1 > hi) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int u = u0 + (i >> 2) * 16 + 4 * j + (i & 3);
-        if (u < lo || u > hi) sc[i] = -INFINITY;
-      }
-    }
-    float cmax = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
-                       fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
-    cmax = head_max(cmax);
-    if (__any(cmax > st.m[c] + RESCALE_SLACK)) {
-      const float mnew = fmaxf(st.m[c], cmax);
-      const float alpha = mnew == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(st.m[c] - mnew);
-      st.l[c] *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt) st.o[dt][c] *= alpha;
-      st.m[c] = mnew;
-    }
-    const float muse = st.m[c] == -INFINITY ? 0.0f : st.m[c];
-    float pv[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      pv[i] = __builtin_amdgcn_exp2f(sc[i] - muse);
-      st.l[c] += pv[i];
-    }
-    bf16x8 ph, pl;
-#pragma unroll
-    for (int i = 0; i < 8; i += 2) {
-      const f32x2 f = {pv[i], pv[i + 1]};
-      const bf16x2 h = __builtin_convertvector(f, bf16x2);
-      const bf16x2 r = __builtin_convertvector(f - __builtin_convertvector(h, f32x2), bf16x2);
-      ph[i] = h[0]; ph[i + 1] = h[1];
-      pl[i] = r[0]; pl[i + 1] = r[1];
-    }
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
-      st.o[dt][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[dt], ph, st.o[dt][c], 0, 0, 0);
-      st.o[dt][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[dt], pl, st.o[dt][c], 0, 0, 0);
-    }
+    tile_step(op, q.op[ct][0][0][lane], q.op[ct][0][1][lane], q.op[ct][1][0][lane],
+              q.op[ct][1][1][lane], u0, lane >> 4, st, c);
   }
 }
 
-// E4M3FN byte of x (OCP format: bias 7, max 448, no infinities), round to
-// nearest even, saturating.  The gfx950 converter rounds to nearest even but
-// turns magnitudes past the last rounding interval into NaN, so values are
-// clamped to +-448 first; NaN stays NaN.
-__device__ __forceinline__ uint8_t to_e4m3(float x) {
-  if (fabsf(x) > 448.0f) x = copysignf(448.0f, x);
-  const int packed = __builtin_amdgcn_cvt_pk_fp8_f32(x, 0.0f, 0, false);
-  return (uint8_t)(packed & 0xff);
-}
-
-// RoPE factors of one block token: pair i (dims i, i+32) turns by
-// theta = fp32(p) * inv_i with inv_i = base^(-i/32) rounded to fp32 (a table
-// the host fills once per call); sin/cos of that fp32 angle are taken in
-// double so large positions keep full accuracy (task page "Gated attention
-// decode", section "What to compute", the rope line; sliding layers only,
-// section "Shapes").  The table is read from the kernel's argument block,
-// whose first member is the StepArgs (a per-lane index into the by-value
-// argument itself would make the compiler copy it to scratch).
-__device__ __forceinline__ float2 rope_cs(int p, int i) {
-  const char *args = (const char *)__builtin_amdgcn_kernarg_segment_ptr();
-  const float *rope_inv = reinterpret_cast<const float *>(args + offsetof(StepArgs, rope_inv));
-  const float inv = rope_inv[i];
-  const float th = (float)p * inv;
-  double sd, cd;
-  sincos((double)th, &sd, &cd);
-  return make_float2((float)cd, (float)sd);
+// Prefill: the wave's two column tiles, Q^T in registers ([tile][K-step]).
+__device__ __forceinline__ void compute_chunk_prefill(const RowBuf2 &rb, int u0, int lane,
+                                                      const bf16x8 (&qh)[2][2],
+                                                      const bf16x8 (&ql)[2][2], VerifyState &st) {
+  const ChunkOps2 op = chunk_ops2(rb);
+#pragma unroll
+  for (int c = 0; c < 2; ++c)
+    tile_step(op, qh[c][0], ql[c][0], qh[c][1], ql[c][1], u0, lane >> 4, st, c);
 }
 
 // Split and QK-norm of one (token, head) query and RoPE on sliding layers
@@ -518,9 +518,12 @@ __device__ __forceinline__ void store_table(const StepArgs &a, const TableIn &in
   }
 }
 
+template <int MODE>
 struct Lds {
+  static constexpr int MAXU = MODE == 3 ? MAX_UNITS : MAX_BATCH;   // plan units
+  static constexpr int NCS = MODE == 3 ? PREFILL_TB : 8;           // tokens per unit
   uint32_t lrows[MAX_SPLIT_LDS];
-  float2 cs[8][32];          // RoPE (cos, sin) per block token and pair
+  float2 cs[NCS][32];        // RoPE (cos, sin) per token of the unit and pair
   union {
     float sm_o[WAVES][HQ][D];   // decode: the 8 waves' O per head
     float mrg[2][64][68];       // verify merge: chunk lane 1's O per KV head and column (padded)
@@ -530,10 +533,10 @@ struct Lds {
   QOps dq;                      // decode: the token's Q^T operands
   float sm_m[WAVES][HQ];
   float sm_l[WAVES][HQ];
-  int pref[MAX_BATCH + 1];
-  int scan[WAVES];            // the plan's per-wave totals
-  int req_len[MAX_BATCH];    // seq_lens[b], kept from the plan
-  int req_p0[MAX_BATCH];     // positions[b * L] (sliding layers)
+  int pref[MAXU + 1];
+  int scan[WAVES];           // the plan's per-wave totals
+  int req_len[MAXU];         // end of each unit's key range (last token's position + 1)
+  int req_p0[MAXU];          // position of each unit's first token (sliding layers)
 };
 
 // One segment: chunks [x, y) of request b's key range (chunk i = keys
@@ -543,7 +546,7 @@ struct Lds {
 // KV head w % 2, column half (w / 2) % 2 and every other chunk from w / 4.
 template <int MODE, int NBUF>
 __device__ __forceinline__ void process_segment(const StepArgs &a, int b, const KeyRange &r, int x,
-                                                int y, int slot, Lds &sh) {
+                                                int y, int slot, Lds<MODE> &sh) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int n = lane & 15, j = lane >> 4;
   const float qmul = a.kv_scale * (LOG2E / 8.0f);
@@ -811,39 +814,169 @@ __device__ __forceinline__ void process_segment(const StepArgs &a, int b, const 
   }
 }
 
+#ifndef MUSEATTN_PREFILL_NBUF
+#define MUSEATTN_PREFILL_NBUF 2
+#endif
+
+// Prefill (L > 8): plan unit = token group blk of request b, block tokens
+// j0 = 16 blk .. j0 + nt - 1.  Wave w takes KV head g = w % 2 and the group's
+// tokens 4qq .. 4qq + 3, qq = w / 2: its column tiles c = 0, 1 hold tokens
+// 4qq + 2c and 4qq + 2c + 1 (lane column n: token 4qq + 2c + n/8, head
+// 8g + n%8), with Q^T in registers.  Every wave walks all chunks of the
+// segment; the four waves of a KV head read the same rows, which the caches
+// serve after the first, so HBM sees each row once per 16 tokens.  The new
+// k/v rows were written by the rows kernel before this kernel started.
+template <int NBUF>
+__device__ __forceinline__ void process_segment_prefill(const StepArgs &a, int b, int blk,
+                                                        const KeyRange &r, int x, int y,
+                                                        int slot, Lds<3> &sh) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int n = lane & 15, j = lane >> 4;
+  const float qmul = a.kv_scale * (LOG2E / 8.0f);
+  const int nseg = y - x;
+  const int npieces = (nseg + PIECE_CHUNKS - 1) / PIECE_CHUNKS;
+  auto piece_x = [&](int pc) { return x + (int)((int64_t)pc * nseg / npieces); };
+  const int g = wave & 1, qq = wave >> 1;
+  const int j0 = blk * a.tb;
+  const int nt = a.L - j0 < a.tb ? a.L - j0 : a.tb;   // tokens in the group
+  auto tok = [&](int c) { return 4 * qq + 2 * c + (n >> 3); };   // the lane column's token
+
+  // One batch: the first piece's table entries, the lane's column tokens'
+  // positions and q rows, the q norm weights.
+  TableIn tin;
+  load_table_in(a, b, r, r.kbase + x * CHUNK, tin);
+  int cpos[2];
+  QIn qin[2];
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const int tk = tok(c);
+    const int t = b * a.L + j0 + (tk < nt ? tk : nt - 1);
+    cpos[c] = a.positions[t];
+    qin[c] = load_q_in(a, t, 8 * g + (n & 7), j);
+  }
+  const f32x4 *w4 = reinterpret_cast<const f32x4 *>(a.wq + 16 * j);
+  const f32x4 wv[4] = {w4[0], w4[1], w4[2], w4[3]};
+  __builtin_amdgcn_sched_barrier(0);
+
+  __syncthreads();   // the previous segment is done with sh.cs and sh.lrows
+  if (a.sliding) {
+    const int tk = tid >> 5;   // 512 threads: 16 tokens x 32 pairs
+    if (tk < nt) sh.cs[tk][tid & 31] = rope_cs(a.positions[b * a.L + j0 + tk], tid & 31);
+    __syncthreads();
+  }
+  store_table(a, tin, sh.lrows);
+
+  bf16x8 qh[2][2], ql[2][2];
+  VerifyState vs;
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const int tk = tok(c);
+    float yq[16];
+    q_values(a, qin[c], wv, j, sh.cs[tk < nt ? tk : nt - 1], yq);
+    pack_q(yq, 0, qmul, qh[c][0], ql[c][0]);
+    pack_q(yq, 1, qmul, qh[c][1], ql[c][1]);
+    // causal bound: the token's position; window: 2047 keys before it
+    const int p = cpos[c];
+    vs.hi[c] = tk < nt ? (p < r.khi ? p : r.khi) : -1;
+    vs.lo[c] = a.sliding ? p - (WINDOW - 1) : 0;
+    vs.m[c] = -INFINITY;
+    vs.l[c] = 0.0f;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) vs.o[dt][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  __syncthreads();   // the first piece's row ids are in LDS
+
+  for (int pc = 0; pc < npieces; ++pc) {
+    const int px = piece_x(pc), py = piece_x(pc + 1);
+    const int nch = py - px;
+    const int kstart = r.kbase + px * CHUNK;
+    if (pc > 0) {
+      __syncthreads();   // every wave is done with the previous rows
+      TableIn tn;
+      load_table_in(a, b, r, kstart, tn);
+      __builtin_amdgcn_sched_barrier(0);
+      store_table(a, tn, sh.lrows);
+      __syncthreads();
+    }
+    // all chunks of the piece, NBUF in flight, loads unconditional (indices
+    // past the end clamped to the last chunk)
+    const int last = nch - 1;
+    RowBuf2 buf[NBUF];
+#pragma unroll
+    for (int k = 0; k < NBUF; ++k)
+      load_rows2(buf[k], a.k_cache, a.v_cache, sh.lrows + (k < last ? k : last) * CHUNK, n, j, g);
+    int i = 0;
+    for (; i + NBUF <= nch; i += NBUF) {
+#pragma unroll
+      for (int k = 0; k < NBUF; ++k) {
+        compute_chunk_prefill(buf[k], kstart + (i + k) * CHUNK, lane, qh, ql, vs);
+        const int inext = i + k + NBUF;
+        load_rows2(buf[k], a.k_cache, a.v_cache, sh.lrows + (inext < last ? inext : last) * CHUNK,
+                   n, j, g);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < NBUF - 1; ++k)
+      if (i + k < nch) compute_chunk_prefill(buf[k], kstart + (i + k) * CHUNK, lane, qh, ql, vs);
+  }
+
+  // every wave writes the partials of its own columns
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const float lsum = head_sum(vs.l[c]);
+    const int tk = tok(c);
+    if (tk < nt) {
+      const size_t e = ((size_t)slot * a.tb + tk) * HQ + 8 * g + (n & 7);
+      if (j == 0) {
+        a.part_ml[e * 2] = vs.m[c];
+        a.part_ml[e * 2 + 1] = lsum;
+      }
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr)
+        *reinterpret_cast<f32x4 *>(a.part_o + e * D + 16 * j + 4 * rr) =
+            f32x4{vs.o[0][c][rr], vs.o[1][c][rr], vs.o[2][c][rr], vs.o[3][c][rr]};
+    }
+  }
+}
+
 // The attention kernel.  Every work-group derives the same plan from the
-// device-side sequence lengths: request b spans chunks [pref[b], pref[b+1]) of
-// the concatenated chunk space, and work-group w takes an equal contiguous
-// share of it (counting each request start as seg_cost chunks), so no
-// work-group idles while another still has a long split.
-// A share that crosses request boundaries is processed one segment per
-// request; segment (w, b) writes its partial to slot w + b (slots are unique
-// because both w and b grow along the chunk space).  The combine kernel then
-// merges each request's slots.
+// device-side sequence lengths: plan unit u (a request, or one token group of
+// a request when L > 8) spans chunks [pref[u], pref[u+1]) of the concatenated
+// chunk space, and work-group w takes an equal contiguous share of it
+// (counting each unit start as seg_cost chunks), so no work-group idles while
+// another still has a long split.  A share that crosses unit boundaries is
+// processed one segment per unit; segment (w, u) writes its partial to slot
+// w + u (slots are unique because both w and u grow along the chunk space).
+// The combine kernel then merges each unit's slots.
 template <int MODE, int NBUF>
 __global__ __launch_bounds__(THREADS, 2) void attn_kernel(StepArgs a) {
-  __shared__ __attribute__((aligned(16))) Lds sh;
+  __shared__ __attribute__((aligned(16))) Lds<MODE> sh;
+  constexpr int MAXU = Lds<MODE>::MAXU;
   const int tid = threadIdx.x;
+  const int NU = a.nunits;
 
-  // chunk-count prefix sums over the requests (RPT per thread, B <= 1024)
-  constexpr int RPT = MAX_BATCH / THREADS;
+  // chunk-count prefix sums over the plan units (RPT per thread)
+  constexpr int RPT = MAXU / THREADS;
   int cnt[RPT], sum = 0;
   {
     // lengths (and, on sliding layers, first positions) of the thread's
-    // requests, loaded as one batch
-    int sl[RPT], p0[RPT];
+    // units, loaded as one batch
+    int sl[RPT], p0[RPT], ublk[RPT];
 #pragma unroll
     for (int k = 0; k < RPT; ++k) {
-      const int b = RPT * tid + k < a.B ? RPT * tid + k : a.B - 1;
-      sl[k] = a.seq_lens[b];
-      p0[k] = a.sliding ? a.positions[b * a.L] : 0;
+      const int u = RPT * tid + k < NU ? RPT * tid + k : NU - 1;
+      int ub;
+      unit_of(a, u, ub, ublk[k]);
+      sl[k] = a.seq_lens[ub];
+      p0[k] = a.sliding ? a.positions[ub * a.L + ublk[k] * a.tb] : 0;
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int k = 0; k < RPT; ++k) {
-      cnt[k] = RPT * tid + k < a.B ? request_chunks(range_from(a, sl[k], p0[k])) : 0;
+      const int len = unit_len(a, sl[k], ublk[k]);
+      cnt[k] = RPT * tid + k < NU ? request_chunks(range_from(a, len, p0[k])) : 0;
       sum += cnt[k];
-      sh.req_len[RPT * tid + k] = sl[k];
+      sh.req_len[RPT * tid + k] = len;
       sh.req_p0[RPT * tid + k] = p0[k];
     }
   }
@@ -868,46 +1001,51 @@ __global__ __launch_bounds__(THREADS, 2) void attn_kernel(StepArgs a) {
     }
 #pragma unroll
     for (int k = 0; k < RPT; ++k) {
-      const int b = RPT * tid + k;
-      if (b < a.B) sh.pref[b] = run;
+      const int u = RPT * tid + k;
+      if (u < NU) sh.pref[u] = run;
       run += cnt[k];
     }
-    if (tid == 0) sh.pref[a.B] = total;
+    if (tid == 0) sh.pref[NU] = total;
   }
   __syncthreads();
-  // Cost space: request b occupies seg_cost units (its segment start-up, in
-  // chunk-equivalents) followed by its chunks, so request b starts at cost
-  // Q_b = pref[b] + b * seg_cost.  Work-groups take equal cost shares; one
-  // whose share covers a request start gets correspondingly fewer chunks.
+  // Cost space: unit u occupies seg_cost units (its segment start-up, in
+  // chunk-equivalents) followed by its chunks, so unit u starts at cost
+  // Q_u = pref[u] + u * seg_cost.  Work-groups take equal cost shares; one
+  // whose share covers a unit start gets correspondingly fewer chunks.
   const int pen = a.seg_cost;
-  const int64_t Ct = (int64_t)sh.pref[a.B] + (int64_t)a.B * pen;
+  const int64_t Ct = (int64_t)sh.pref[NU] + (int64_t)NU * pen;
   const int w = blockIdx.x;
   const int G = Ct < a.work_groups ? (int)Ct : a.work_groups;
   if (w == 0) {
     // the plan, for the combine kernel: chunk prefix sums and work-groups used
-    for (int i = tid; i <= a.B; i += THREADS) a.plan[i] = sh.pref[i];
-    if (tid == 0) a.plan[a.B + 1] = G;
+    for (int i = tid; i <= NU; i += THREADS) a.plan[i] = sh.pref[i];
+    if (tid == 0) a.plan[NU + 1] = G;
   }
   if (w >= G) return;   // uniform over the work-group
   const int64_t cb = (int64_t)w * Ct / G, ce = (int64_t)(w + 1) * Ct / G;
-  auto cost_of = [&](int bb) { return (int64_t)sh.pref[bb] + (int64_t)bb * pen; };
-  int b = 0;
+  auto cost_of = [&](int uu) { return (int64_t)sh.pref[uu] + (int64_t)uu * pen; };
+  int u = 0;
   {
-    int hi = a.B - 1;
-    while (b < hi) {   // largest b whose cost range starts at or before cb
-      const int mid = (b + hi + 1) >> 1;
-      if (cost_of(mid) <= cb) b = mid; else hi = mid - 1;
+    int hi = NU - 1;
+    while (u < hi) {   // largest u whose cost range starts at or before cb
+      const int mid = (u + hi + 1) >> 1;
+      if (cost_of(mid) <= cb) u = mid; else hi = mid - 1;
     }
   }
-  for (; b < a.B && cost_of(b) < ce; ++b) {
-    const int64_t q0 = cost_of(b) + pen;            // cost of chunk 0 of request b
-    const int64_t nb = sh.pref[b + 1] - sh.pref[b];
+  for (; u < NU && cost_of(u) < ce; ++u) {
+    const int64_t q0 = cost_of(u) + pen;            // cost of chunk 0 of unit u
+    const int64_t nb = sh.pref[u + 1] - sh.pref[u];
     const int64_t xs = cb - q0, ys = ce - q0;
     const int x = (int)(xs > 0 ? xs : 0);
     const int y = (int)(ys < nb ? ys : nb);
     if (y <= x) continue;
-    const KeyRange r = range_from(a, sh.req_len[b], sh.req_p0[b]);
-    process_segment<MODE, NBUF>(a, b, r, x, y, w + b, sh);
+    const KeyRange r = range_from(a, sh.req_len[u], sh.req_p0[u]);
+    int b, blk;
+    unit_of(a, u, b, blk);
+    if constexpr (MODE == 3)
+      process_segment_prefill<NBUF>(a, b, blk, r, x, y, w + u, sh);
+    else
+      process_segment<MODE, NBUF>(a, b, r, x, y, w + u, sh);
   }
 }
 
@@ -915,8 +1053,10 @@ void launch_attn(const StepArgs &a, hipStream_t stream) {
   const dim3 grid(a.work_groups), block(THREADS);
   if (a.L == 1)
     hipLaunchKernelGGL((attn_kernel<0, MUSEATTN_DECODE_NBUF>), grid, block, 0, stream, a);
-  else
+  else if (a.L <= 8)
     hipLaunchKernelGGL((attn_kernel<2, MUSEATTN_VERIFY_NBUF>), grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL((attn_kernel<3, MUSEATTN_PREFILL_NBUF>), grid, block, 0, stream, a);
 }
 
 }  // namespace museattn

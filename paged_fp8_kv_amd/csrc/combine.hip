@@ -21,23 +21,26 @@ __global__ __launch_bounds__(256) void combine_kernel(StepArgs a) {
   const int th = blockIdx.x;          // t * 16 + h
   const int t = th / HQ, h = th % HQ;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int b = t / a.L, jt = t % a.L;
-  const int64_t p0 = a.plan[b], p1 = a.plan[b + 1];
-  const int G = a.plan[a.B + 1];
-  const int64_t Ct = (int64_t)a.plan[a.B] + (int64_t)a.B * a.seg_cost;
+  // token t = block token jl of request b, token jt of plan unit u
+  const int b = t / a.L, jl = t % a.L;
+  const int blk = jl / a.tb, jt = jl - blk * a.tb;
+  const int u = b * a.nblk + blk, NU = a.nunits;
+  const int64_t p0 = a.plan[u], p1 = a.plan[u + 1];
+  const int G = a.plan[NU + 1];
+  const int64_t Ct = (int64_t)a.plan[NU] + (int64_t)NU * a.seg_cost;
   const float g = bf16_bits_to_f32(a.qkv[(size_t)t * QKV_W + G_OFF + h * D + lane]);
   const float wo = a.wo[lane];
-  // slots of request b: w + b for the work-groups w whose cost share meets its
-  // chunks (chunk c of request b sits at cost p0 + (b + 1) * seg_cost + c)
+  // slots of unit u: w + u for the work-groups w whose cost share meets its
+  // chunks (chunk c of unit u sits at cost p0 + (u + 1) * seg_cost + c)
   int s0 = 0, s1 = -1;
   if (p1 > p0) {
-    const int64_t q0 = p0 + (int64_t)(b + 1) * a.seg_cost;
-    s0 = wg_of_chunk(q0, Ct, G) + b;
-    s1 = wg_of_chunk(q0 + (p1 - p0) - 1, Ct, G) + b;
+    const int64_t q0 = p0 + (int64_t)(u + 1) * a.seg_cost;
+    s0 = wg_of_chunk(q0, Ct, G) + u;
+    s1 = wg_of_chunk(q0 + (p1 - p0) - 1, Ct, G) + u;
   }
   const float2 *ml = reinterpret_cast<const float2 *>(a.part_ml);
   const f32x4 *po = reinterpret_cast<const f32x4 *>(a.part_o);
-  auto entry = [&](int s) { return ((size_t)s * a.L + jt) * HQ + h; };
+  auto entry = [&](int s) { return ((size_t)s * a.tb + jt) * HQ + h; };
 
   // online merge of slots s0 + sl, s0 + sl + 16, ... (four loads in flight)
   const int sl = tid >> 4, dq = tid & 15;

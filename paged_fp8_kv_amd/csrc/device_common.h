@@ -18,6 +18,9 @@ constexpr int CHUNK = 32;    // keys per step of the attention kernel's inner lo
 constexpr int WAVES = 8;     // waves per attention work-group (one work-group per CU)
 constexpr int THREADS = 64 * WAVES;
 constexpr int MAX_BATCH = 1024;   // requests per call (prefix sums live in LDS)
+constexpr int PREFILL_TB = 16;    // block tokens per plan unit when L > 8 (prefill)
+constexpr int MAX_L = 16384;      // block tokens per request
+constexpr int MAX_UNITS = 4096;   // plan units (B * ceil(L / 16)) of a prefill call
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -45,7 +48,23 @@ struct StepArgs {
   int work_groups;         // attention work-groups launched (each takes an equal
                            // share of all requests' key chunks)
   int seg_cost;            // chunk-equivalents one segment start-up costs
+  // Plan units: request b's block tokens in groups of tb (unit u = b * nblk +
+  // blk holds tokens blk*tb ..); one group per request (tb = L) up to L = 8.
+  int tb, nblk, nunits;
 };
+
+// Request and token group of plan unit u.
+__device__ __forceinline__ void unit_of(const StepArgs &a, int u, int &b, int &blk) {
+  b = u / a.nblk;
+  blk = u - b * a.nblk;
+}
+
+// Key positions of unit u's union range end at this length (its last token's
+// position + 1): seq_len_b - L + min(L, (blk + 1) tb).
+__device__ __forceinline__ int unit_len(const StepArgs &a, int seq_len, int blk) {
+  const int end = (blk + 1) * a.tb;
+  return seq_len - a.L + (end < a.L ? end : a.L);
+}
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t h) {
   return __uint_as_float(((uint32_t)h) << 16);
@@ -141,6 +160,34 @@ __device__ __forceinline__ float wave_max(float x) {
   xi = __float_as_int(x);
   auto q = __builtin_amdgcn_permlane32_swap(xi, xi, false, false);
   return fmaxf(__int_as_float(q[0]), __int_as_float(q[1]));
+}
+
+// E4M3FN byte of x (OCP format: bias 7, max 448, no infinities), round to
+// nearest even, saturating.  The gfx950 converter rounds to nearest even but
+// turns magnitudes past the last rounding interval into NaN, so values are
+// clamped to +-448 first; NaN stays NaN.
+__device__ __forceinline__ uint8_t to_e4m3(float x) {
+  if (fabsf(x) > 448.0f) x = copysignf(448.0f, x);
+  const int packed = __builtin_amdgcn_cvt_pk_fp8_f32(x, 0.0f, 0, false);
+  return (uint8_t)(packed & 0xff);
+}
+
+// RoPE factors of one block token: pair i (dims i, i+32) turns by
+// theta = fp32(p) * inv_i with inv_i = base^(-i/32) rounded to fp32 (a table
+// the host fills once per call); sin/cos of that fp32 angle are taken in
+// double so large positions keep full accuracy (task page "Gated attention
+// decode", section "What to compute", the rope line; sliding layers only,
+// section "Shapes").  The table is read from the kernel's argument block,
+// whose first member is the StepArgs (a per-lane index into the by-value
+// argument itself would make the compiler copy it to scratch).
+__device__ __forceinline__ float2 rope_cs(int p, int i) {
+  const char *args = (const char *)__builtin_amdgcn_kernarg_segment_ptr();
+  const float *rope_inv = reinterpret_cast<const float *>(args + offsetof(StepArgs, rope_inv));
+  const float inv = rope_inv[i];
+  const float th = (float)p * inv;
+  double sd, cd;
+  sincos((double)th, &sd, &cd);
+  return make_float2((float)cd, (float)sd);
 }
 
 }  // namespace museattn

@@ -6,4 +6,5 @@
 namespace museattn {
 void launch_attn(const StepArgs &a, hipStream_t stream);
 void launch_combine(const StepArgs &a, hipStream_t stream);
+void launch_rows(const StepArgs &a, hipStream_t stream);
 }  // namespace museattn

@@ -30,15 +30,22 @@ struct Layout {
   size_t plan_off, ml_off, o_off, total;
 };
 
+// Plan units: up to 8 block tokens a request is one unit; beyond (prefill)
+// its tokens form groups of PREFILL_TB.
+int unit_tokens(int L) { return L <= 8 ? L : PREFILL_TB; }
+int units_per_request(int L) { return (L + unit_tokens(L) - 1) / unit_tokens(L); }
+
 Layout layout(int B, int L, int work_groups) {
   Layout ly;
   ly.work_groups = work_groups;
-  const size_t slots = (size_t)work_groups + B;   // partial slots w + b
+  const size_t units = (size_t)B * units_per_request(L);
+  const size_t slots = (size_t)work_groups + units;   // partial slots w + u
+  const size_t tb = unit_tokens(L);
   auto al = [](size_t x) { return (x + 255) / 256 * 256; };
   ly.plan_off = 0;
-  ly.ml_off = ly.plan_off + al(((size_t)B + 2) * sizeof(int));
-  ly.o_off = ly.ml_off + al(slots * L * HQ * 2 * sizeof(float));
-  ly.total = ly.o_off + al(slots * L * HQ * D * sizeof(float));
+  ly.ml_off = ly.plan_off + al((units + 2) * sizeof(int));
+  ly.o_off = ly.ml_off + al(slots * tb * HQ * 2 * sizeof(float));
+  ly.total = ly.o_off + al(slots * tb * HQ * D * sizeof(float));
   return ly;
 }
 
@@ -46,8 +53,9 @@ int check_shapes(int B, int L, int max_seq_len, int page_size, int layer_kind,
                  const museattn_params *params) {
   if (page_size != 1 && page_size != 64) return MUSEATTN_ERR_PAGE_SIZE;
   if (layer_kind != MUSEATTN_FULL && layer_kind != MUSEATTN_SLIDING) return MUSEATTN_ERR_LAYER_KIND;
-  if (B < 1 || B > MAX_BATCH || L < 1 || L > 8 || max_seq_len < L || max_seq_len > MAX_SEQ)
+  if (B < 1 || B > MAX_BATCH || L < 1 || L > MAX_L || max_seq_len < L || max_seq_len > MAX_SEQ)
     return MUSEATTN_ERR_SHAPE;
+  if ((int64_t)B * units_per_request(L) > MAX_UNITS) return MUSEATTN_ERR_SHAPE;
   if (params == nullptr) return MUSEATTN_ERR_NULL;
   if (params->work_groups < 0 || params->work_groups > MAX_WORK_GROUPS) return MUSEATTN_ERR_PARAM;
   return MUSEATTN_OK;
@@ -68,7 +76,8 @@ const char *museattn_strerror(int status) {
     case MUSEATTN_ERR_NULL: return "a required pointer is null";
     case MUSEATTN_ERR_PAGE_SIZE: return "page_size must be 1 or 64";
     case MUSEATTN_ERR_LAYER_KIND: return "layer_kind must be MUSEATTN_FULL or MUSEATTN_SLIDING";
-    case MUSEATTN_ERR_SHAPE: return "B, L, max_seq_len or num_rows out of range";
+    case MUSEATTN_ERR_SHAPE:
+      return "B, L, B * ceil(L / 16) (L > 8), max_seq_len or num_rows out of range";
     case MUSEATTN_ERR_TABLE: return "table_stride < ceil(max_seq_len / page_size)";
     case MUSEATTN_ERR_ALIGN: return "misaligned pointer (caches need 16-byte alignment)";
     case MUSEATTN_ERR_WORKSPACE: return "workspace too small or not 256-byte aligned";
@@ -168,10 +177,14 @@ int museattn_attn_step_profiled(const void *qkv, const int32_t *positions, const
   a.work_groups = ly.work_groups;
   // a segment start-up (batch of loads + first rows) is worth about this many
   // 32-key chunks of one work-group's streaming (measured on MI355X)
-  a.seg_cost = L == 1 ? 14 : 4;
+  a.seg_cost = L == 1 ? 14 : (L <= 8 ? 4 : 2);
+  a.tb = unit_tokens(L);
+  a.nblk = units_per_request(L);
+  a.nunits = B * a.nblk;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();   // clear an error left by earlier, unrelated calls
+  if (L > 8) launch_rows(a, s);   // prefill: every new row before any attention
   if (attn_start_event) (void)hipEventRecord(static_cast<hipEvent_t>(attn_start_event), s);
   launch_attn(a, s);
   if (attn_end_event) (void)hipEventRecord(static_cast<hipEvent_t>(attn_end_event), s);

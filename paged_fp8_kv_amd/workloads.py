@@ -23,7 +23,12 @@ defined beyond a sentence each; the draws below stand in for them:
              enlarged 6-fold (clipped): on sliding layers the first visible
              position of each block token's window and the one just outside
              it, on full layers positions 0 and 1; on both, the last two cached
-             positions.
+             positions;
+  outliers   (named by the prefill page's tests, not defined there) -- soft
+             draws with one key element in 64 enlarged 8-fold (then clipped):
+             extreme scores for the softmax; values stay soft (an outlier
+             value can put a head's output near 8 after the output norm,
+             where bf16 rounding alone exceeds the output bar).
 """
 from __future__ import annotations
 
@@ -127,6 +132,12 @@ class Workload:
             edge += [n - 2, n - 1]
             for u in sorted({u for u in edge if 0 <= u < n}):
                 x[:, u] *= 6.0
+            x = x.reshape(-1)
+        elif self.dist == "outliers":
+            ro = np.random.Generator(np.random.PCG64([self.seed, src, 2]))
+            x = x.reshape(2, -1)
+            pick = ro.random(x.shape[1]) < 1.0 / 64.0
+            x[0] = np.where(pick, x[0] * 8.0, x[0])
             x = x.reshape(-1)
         elif self.dist != "soft":
             raise ValueError(f"unknown distribution {self.dist!r}")

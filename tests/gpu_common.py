@@ -71,7 +71,7 @@ def check_bytes(w: W.Workload, kb_gpu, vb_gpu):
     return float((dk == 0).mean())
 
 
-def oracle_out(w: W.Workload, kb_gpu, vb_gpu, pools=None):
+def oracle_out(w: W.Workload, kb_gpu, vb_gpu, pools=None, tokens=None):
     """Oracle output attending to the GPU's new entries.  pools: host pools
     (numpy) or None for a logical pool of w's requests."""
     if pools is None:
@@ -82,7 +82,8 @@ def oracle_out(w: W.Workload, kb_gpu, vb_gpu, pools=None):
     out, _, _ = O.attn_step(w.qkv.float().numpy(), w.positions, w.table, kp, vp, B=w.B, L=w.L,
                             page_size=w.page_size, layer_kind=w.layer_kind,
                             kv_scale=w.kv_scale, w_q=w.w_q, w_k=w.w_k, w_o=w.w_o, eps=EPS,
-                            q_scale=QS, rope_base=ROPE_BASE, new_rows=(kb_gpu, vb_gpu))
+                            q_scale=QS, rope_base=ROPE_BASE, new_rows=(kb_gpu, vb_gpu),
+                            tokens=tokens)
     return out
 
 
@@ -95,15 +96,19 @@ def compare_out(got: np.ndarray, want: np.ndarray, label: str):
     return mx, mean
 
 
-def full_check(w: W.Workload, d: dict, requests=None, host_pools=None):
+def full_check(w: W.Workload, d: dict, requests=None, host_pools=None, tokens=None):
     """Bytes and output of a finished GPU step against the oracle.  requests:
-    subset of requests whose outputs the oracle recomputes (None = all)."""
+    subset of requests whose outputs the oracle recomputes (None = all);
+    tokens: block-token indices compared (None = all)."""
     kb_gpu, vb_gpu = gpu_new_bytes(w, d)
     exact = check_bytes(w, kb_gpu, vb_gpu)
     got = d["out"].float().cpu().numpy()
     if requests is None:
-        want = oracle_out(w, kb_gpu, vb_gpu, host_pools)
-        return compare_out(got, want, f"{w.name} (exact k bytes {exact:.4f})")
+        want = oracle_out(w, kb_gpu, vb_gpu, host_pools, tokens)
+        if tokens is not None:
+            got, want = got[:, tokens], want[:, tokens]
+        label = f"{w.name} (exact k bytes {exact:.4f})" + ("" if tokens is None else f" tokens {list(tokens)[:6]}..")
+        return compare_out(got, want, label)
     sub = w.subset(requests)
     sel = np.array([[b * w.L + j for j in range(w.L)] for b in requests]).reshape(-1)
     want = oracle_out(sub, kb_gpu[sel], vb_gpu[sel], None)

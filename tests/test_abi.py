@@ -67,6 +67,8 @@ def test_valid_arguments_pass():
     assert _check(L=8, layer_kind=P.SLIDING) == 0
     assert _check(work_groups=65535) == 0
     assert _check(B=1024) == 0
+    assert _check(L=753, max_seq_len=2000, table_stride=2000) == 0          # prefill block
+    assert _check(B=4, L=16384, max_seq_len=20000, table_stride=20000) == 0  # 4 x 1024 groups
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -75,7 +77,9 @@ def test_valid_arguments_pass():
     (dict(ws=0), -1),
     (dict(page_size=16), -2),
     (dict(layer_kind=2), -3),
-    (dict(L=9), -4),
+    (dict(L=16385, max_seq_len=20000), -4),
+    (dict(B=300, L=753, max_seq_len=2000), -4),   # 300 x 48 token groups > 4096
+    (dict(B=5, L=16384, max_seq_len=20000), -4),
     (dict(L=0), -4),
     (dict(B=0), -4),
     (dict(max_seq_len=0), -4),
@@ -111,7 +115,11 @@ def test_workspace_and_launch_shape():
     # independent of the context length (the plan is made on the device)
     assert P.workspace_bytes(4, 8, 1 << 20, 1, P.SLIDING) == P.workspace_bytes(4, 8, 4096, 1, P.SLIDING)
     with pytest.raises(ValueError):
-        P.workspace_bytes(1, 9, 100, 1, P.FULL)
+        P.workspace_bytes(1, 16385, 20000, 1, P.FULL)
+    # prefill: partial slots per 16-token group
+    n = P.workspace_bytes(1, 753, 81000, 1, P.FULL)
+    units = 48
+    assert n >= (units + 2) * 4 + (256 + units) * 16 * 16 * 66 * 4
 
 
 def test_attn_step_refuses_cpu_tensors():

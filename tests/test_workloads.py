@@ -44,3 +44,15 @@ def test_edges_enlarge_only_the_edge_rows():
     full = W.make("e", 9, 1, 1, ctx, W.FULL, 1, 1.0, dist="edges")
     kf, _ = (_vals(x) for x in full.cache_values(0))
     assert np.abs(kf[0]).mean() > 3 * np.abs(ks[0]).mean()
+
+
+def test_outliers_enlarge_keys_only():
+    soft = W.make("o", 10, 1, 1, 4000, W.FULL, 1, 1.0)
+    out = W.make("o", 10, 1, 1, 4000, W.FULL, 1, 1.0, dist="outliers")
+    ks, vs = (_vals(x) for x in soft.cache_values(0))
+    ko, vo = (_vals(x) for x in out.cache_values(0))
+    assert np.array_equal(vs, vo)
+    frac = float(np.mean(ks != ko))
+    assert 0.005 < frac < 0.03   # about one element in 64
+    # |x| >= 6 is ~1e-9 likely for N(0,1), ~0.7% for an 8-fold draw in one element of 64
+    assert np.mean(np.abs(ko) >= 6) > 0.003 and np.mean(np.abs(ks) >= 6) < 1e-4
