@@ -35,6 +35,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "attn_kernel_decode_b32_full_ctx60k-100k_pmc.txt")
 ATTN_SOURCE = os.path.join(ROOT, "paged_fp8_kv_amd", "csrc", "attn_splitk.hip")
 
@@ -85,14 +86,18 @@ def read_traffic(bytes_per_launch_alg):
         return None
 
 
-def cpu_baseline(w, sample_requests: int):
-    """The oracle (as it stands) on a sample of the workload's requests."""
+def cpu_baseline(w, sample_requests: int, sample_tokens: int):
+    """The oracle (as it stands) on a sample of the workload's requests; for a
+    prefill block, on evenly spaced block tokens of request 0."""
     import numpy as np
     from oracle import museattn_oracle as O
     from paged_fp8_kv_amd import workloads as W
 
-    req = list(range(min(sample_requests, w.B)))
+    req = list(range(min(sample_requests, w.B))) if w.L <= 8 else [0]
     sub = w.subset(req)
+    tokens = None
+    if w.L > 8:
+        tokens = sorted({int(x) for x in np.linspace(0, w.L - 1, min(sample_tokens, w.L))})
     log(f"cpu_baseline: building the oracle's view of requests {req[0]}..{req[-1]}")
     kp = W.LogicalPool(sub, range(sub.B), "k")
     vp = W.LogicalPool(sub, range(sub.B), "v")
@@ -106,16 +111,28 @@ def cpu_baseline(w, sample_requests: int):
     O.attn_step(sub.qkv.float().numpy(), sub.positions, sub.table, kp, vp, B=sub.B, L=sub.L,
                 page_size=sub.page_size, layer_kind=sub.layer_kind, kv_scale=sub.kv_scale,
                 w_q=sub.w_q, w_k=sub.w_k, w_o=sub.w_o, eps=float(np.float32(1e-6)),
-                q_scale=float(np.float32(5.473)))
+                q_scale=float(np.float32(5.473)), tokens=tokens)
     dt = time.perf_counter() - t0
-    frac = sub.kv_bytes / w.kv_bytes
+    if tokens is None:
+        frac = sub.kv_bytes / w.kv_bytes
+        what = f"requests 0..{req[-1]} ({sub.B} of {w.B}"
+    else:
+        p = sub.positions[tokens].astype(np.int64)
+        keys = p + 1 if w.layer_kind == 0 else np.minimum(p + 1, 2048)
+        frac = float(keys.sum()) * 16 * 64 * 4 / w.attn_flops
+        what = (f"{len(tokens)} evenly spaced block tokens of request 0 (all {w.L} new rows "
+                f"written and the keys they see dequantised once")
     step_s = dt / frac
     log(f"cpu_baseline: {dt:.2f} s for {sub.kv_bytes / 1e6:.1f} MB of K+V -> {step_s:.2f} s/step")
-    return {"value": round(w.kv_bytes / step_s / 1e9, 4), "unit": "GB/s", "cores": int(threads),
+    if tokens is None:
+        value, unit = round(w.kv_bytes / step_s / 1e9, 4), "GB/s"
+    else:
+        value, unit = round(w.attn_flops / step_s / 1e12, 6), "TFLOP/s"
+    return {"value": value, "unit": unit, "cores": int(threads),
             "kind": "oracle",
-            "sample": f"requests 0..{req[-1]} ({sub.B} of {w.B}, {frac * 100:.1f}% of the step's "
-                      f"K+V bytes), float64 numpy oracle, {dt:.2f} s; scaled to one step "
-                      f"({step_s:.2f} s/step)"}
+            "sample": f"{what}, {frac * 100:.2f}% of the step's "
+                      f"{'K+V bytes' if tokens is None else 'attention FLOPs'}), float64 numpy "
+                      f"oracle, {dt:.2f} s; scaled to one step ({step_s:.2f} s/step)"}
 
 
 def main():
@@ -123,7 +140,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="2", help="workload id (0, 1, 2, 3s, 3f, 4)")
+    ap.add_argument("--config", default="2",
+                    help="workload id (0, 1, 2, 3s, 3f, 4; prefill blocks pf1f, pf1s, pf4f, "
+                         "pf4s, pff0, pfs32, pff32, pff64)")
     ap.add_argument("--work-groups", type=int, default=0,
                     help="attention work-groups (0 = the library's choice)")
     ap.add_argument("--pool-rows", type=int, default=0,
@@ -131,6 +150,8 @@ def main():
     ap.add_argument("--cold-reps", type=int, default=200,
                     help="graph replays timed one by one after a 1 GiB cache flush")
     ap.add_argument("--cpu-sample", type=int, default=16, help="requests the oracle times")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=96,
+                    help="block tokens the oracle times (prefill blocks)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true",
                     help="time K eager calls instead of one replay of K captured steps")
@@ -290,33 +311,53 @@ def main():
         del flush
 
     kv = w.kv_bytes
-    value = kv / (ms_per_step * 1e-3) / 1e9
-    achieved = kv / (attn_avg_ms * 1e-3) / 1e9
-    traffic = read_traffic(kv)
-    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": traffic, "kernel": "attn_kernel (q/k norm, cache write, split-K attention)",
-                "algorithmic_bytes_per_launch": kv, "avg_launch_us": round(attn_avg_ms * 1e3, 2),
-                "avg_launch_us_from": f"HIP events around each of {args.steps} eager launches"}
+    timing_note = f"HIP events around each of {args.steps} eager launches"
+    if w.L <= 8:
+        # decode and verify read every visible key's 256 bytes once: HBM-bound
+        value = kv / (ms_per_step * 1e-3) / 1e9
+        unit, peak = "GB/s", HBM_PEAK_GBS
+        metric = "us/step and achieved HBM GB/s (% peak), decode-32 full-attn ctx 80K, 1 GPU"
+        achieved = kv / (attn_avg_ms * 1e-3) / 1e9
+        traffic = read_traffic(kv) if w.L == 1 else None
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": peak,
+                    "unit": unit, "frac": round(achieved / peak, 4), "traffic": traffic,
+                    "kernel": "attn_kernel (q/k norm, cache write, split-K attention)",
+                    "algorithmic_bytes_per_launch": kv,
+                    "avg_launch_us": round(attn_avg_ms * 1e3, 2), "avg_launch_us_from": timing_note}
+    else:
+        # a prefill block: 4 * 64 FLOPs per (visible key, token, query head), a
+        # bf16 MFMA contraction; each key's bytes are reused by up to L tokens
+        fl = w.attn_flops
+        value = fl / (ms_per_step * 1e-3) / 1e12
+        unit, peak = "TFLOP/s", MFMA_BF16_PEAK_TFLOPS
+        metric = "us/step and attention TFLOP/s (% of bf16 MFMA peak), prefill block, 1 GPU"
+        achieved = fl / (attn_avg_ms * 1e-3) / 1e12
+        roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
+                    "unit": unit, "frac": round(achieved / peak, 4), "traffic": None,
+                    "kernel": "attn_kernel (split-K causal block attention; the new rows are "
+                              "written by rows_kernel before it)",
+                    "algorithmic_flops_per_launch": fl,
+                    "avg_launch_us": round(attn_avg_ms * 1e3, 2), "avg_launch_us_from": timing_note}
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, args.cpu_sample)
+        cpu = cpu_baseline(w, args.cpu_sample, args.cpu_sample_tokens)
 
     line = {
-        "metric": "us/step and achieved HBM GB/s (% peak), decode-32 full-attn ctx 80K, 1 GPU",
-        "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "metric": metric,
+        "value": round(value, 2 if w.L > 8 else 1), "unit": unit, "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
         "us_per_step": round(ms_per_step * 1e3, 2), "timing": mode,
         "graph_warmup_steps": (max(1, -(-args.graph_warmup // args.steps)) * args.steps
-                               if mode == "graph" else 0), "pct_peak": round(100 * value / HBM_PEAK_GBS, 2),
+                               if mode == "graph" else 0), "pct_peak": round(100 * value / peak, 2),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "kv_dtype": "fp8_e4m3fn", "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "L": w.L, "layer": "full" if w.layer_kind == 0
                    else "sliding", "page_size": w.page_size, "kv_scale": w.kv_scale,
                    "ctx_min": int(w.ctx.min()), "ctx_max": int(w.ctx.max()),
                    "ctx_mean": round(float(w.ctx.mean()), 1), "keys": int(kv // 256),
-                   "kv_bytes": kv, "pool_rows": w.num_rows, "seed": w.seed,
+                   "kv_bytes": kv, "attn_flops": w.attn_flops, "pool_rows": w.num_rows,
+                   "seed": w.seed,
                    "work_groups": P.work_groups(w.B, w.L, w.max_seq_len, w.layer_kind,
                                                 args.work_groups)},
         "cold_cache_graph_replay": cold,

@@ -81,8 +81,9 @@ enum museattn_status {
                                      (L > 8) above 4096, max_seq_len or
                                      num_rows out of range */
   MUSEATTN_ERR_TABLE = -5,        /* table_stride < ceil(max_seq_len / page_size) */
-  MUSEATTN_ERR_ALIGN = -6,        /* k_cache/v_cache not 16-byte aligned, or
-                                     qkv/out/weights not naturally aligned */
+  MUSEATTN_ERR_ALIGN = -6,        /* k_cache, v_cache, qkv or a norm weight not
+                                     16-byte aligned, out not 8-byte aligned,
+                                     positions/table/seq_lens not 4-byte aligned */
   MUSEATTN_ERR_WORKSPACE = -7,    /* workspace smaller than museattn_workspace_bytes()
                                      or not 256-byte aligned */
   MUSEATTN_ERR_PARAM = -8,        /* kv_scale, eps, q_scale, rope_base or
@@ -94,9 +95,12 @@ enum museattn_status {
 /* Constants of the step that the page fixes or that the computation needs
  * but the page's input list leaves implicit (all read on the host). */
 typedef struct museattn_params {
-  const float *q_norm_w;   /* device float32 [64]: per-dim weight of q's rmsnorm */
-  const float *k_norm_w;   /* device float32 [64]: per-dim weight of k's rmsnorm */
-  const float *o_norm_w;   /* device float32 [64]: per-dim weight of the output rmsnorm */
+  const float *q_norm_w;   /* device float32 [64], 16-byte aligned: per-dim weight of
+                              q's rmsnorm */
+  const float *k_norm_w;   /* device float32 [64], 16-byte aligned: per-dim weight of
+                              k's rmsnorm */
+  const float *o_norm_w;   /* device float32 [64], 16-byte aligned: per-dim weight of
+                              the output rmsnorm */
   float eps;               /* rmsnorm epsilon, >= 0 (1e-6) */
   float q_scale;           /* multiplier of the normed q (5.473) */
   float rope_base;         /* RoPE base, > 0 (10000) */
@@ -122,7 +126,7 @@ int museattn_check_args(const void *qkv, const int32_t *positions, const int32_t
                         size_t workspace_bytes);
 
 /* One attention step (the operation described at the top of this file).
- *   qkv        bf16 [B*L][2304], row t = b*L + j
+ *   qkv        bf16 [B*L][2304], row t = b*L + j, 16-byte aligned
  *   positions  int32 [B*L], p of token t (normally seq_lens[b] - L + j)
  *   table      int32 [B][table_stride]: rows (page_size 1) or page ids (64)
  *   seq_lens   int32 [B]: cached tokens + L ("FA3 lengths"), <= max_seq_len
@@ -132,7 +136,7 @@ int museattn_check_args(const void *qkv, const int32_t *positions, const int32_t
  *   kv_scale   > 0: stored byte = fp8(x / kv_scale); read value = byte * kv_scale
  *   page_size  1 or 64
  *   layer_kind MUSEATTN_FULL or MUSEATTN_SLIDING
- *   out        bf16 [B][L][1024]
+ *   out        bf16 [B][L][1024], 8-byte aligned
  *   stream     hipStream_t the work is enqueued on (NULL = default stream)
  *   1 <= B <= 1024, 1 <= L <= 16384 with B * ceil(L / 16) <= 4096 when L > 8
  *   (up to 8 block tokens the new rows are written inside the attention

@@ -4,11 +4,15 @@
 // (task page "Gated attention decode", section "What to compute", last line
 // of the listing; output shape from the same section).
 //
-// One 256-thread work-group per (token, head).  The plan entries, the gate
-// and the output-norm weight are loaded as one batch; then 16 slot lanes x 16
-// dimension quads each merge their slots online (running max, rescaled sum
-// and output), so the partials take a single memory round trip; LDS merges
-// the 16 slot lanes and one wave finishes the gated norm.
+// Decode and verify blocks (many slots per token): one 256-thread work-group
+// per (token, head).  The plan entries, the gate and the output-norm weight
+// are loaded as one batch; then 16 slot lanes x 16 dimension quads each merge
+// their slots online (running max, rescaled sum and output), so the partials
+// take a single memory round trip; LDS merges the 16 slot lanes and one wave
+// finishes the gated norm.
+//
+// Prefill blocks (thousands of tokens, a few slots each): one work-group per
+// token, 16 lanes per head, each lane merging all slots for 4 dimensions.
 #include "device_common.h"
 #include "launch.h"
 
@@ -99,8 +103,80 @@ __global__ __launch_bounds__(256) void combine_kernel(StepArgs a) {
   }
 }
 
+// Prefill merge: work-group t = token t; lane group hg = lane / 16 of wave w
+// takes head h = 4w + hg, lane dq = lane % 16 its dims 4dq..4dq+3.  All heads
+// of a token share its unit's slots.
+__global__ __launch_bounds__(256) void combine_tokens_kernel(StepArgs a) {
+  const int t = blockIdx.x;
+  const int tid = threadIdx.x, h = tid >> 4, dq = tid & 15;
+  const int b = t / a.L, jl = t % a.L;
+  const int blk = jl / a.tb, jt = jl - blk * a.tb;
+  const int u = b * a.nblk + blk, NU = a.nunits;
+  const int64_t p0 = a.plan[u], p1 = a.plan[u + 1];
+  const int G = a.plan[NU + 1];
+  const int64_t Ct = (int64_t)a.plan[NU] + (int64_t)NU * a.seg_cost;
+  const uint2 graw = *reinterpret_cast<const uint2 *>(a.qkv + (size_t)t * QKV_W + G_OFF + h * D +
+                                                      4 * dq);
+  const f32x4 wo = *reinterpret_cast<const f32x4 *>(a.wo + 4 * dq);
+  int s0 = 0, s1 = -1;
+  if (p1 > p0) {
+    const int64_t q0 = p0 + (int64_t)(u + 1) * a.seg_cost;
+    s0 = wg_of_chunk(q0, Ct, G) + u;
+    s1 = wg_of_chunk(q0 + (p1 - p0) - 1, Ct, G) + u;
+  }
+  const float2 *ml = reinterpret_cast<const float2 *>(a.part_ml);
+  const f32x4 *po = reinterpret_cast<const f32x4 *>(a.part_o);
+  auto entry = [&](int s) { return ((size_t)s * a.tb + jt) * HQ + h; };
+
+  float m = -INFINITY, l = 0.0f;
+  f32x4 o = {0.f, 0.f, 0.f, 0.f};
+  auto merge = [&](float2 v, f32x4 x) {
+    const float mn = fmaxf(m, v.x);
+    const float c0 = m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m - mn);
+    const float c1 = v.x == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(v.x - mn);
+    l = l * c0 + v.y * c1;
+    o = o * c0 + x * c1;
+    m = mn;
+  };
+  int s = s0;
+  for (; s + 3 <= s1; s += 4) {
+    float2 v[4];
+    f32x4 x[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const size_t e = entry(s + k);
+      v[k] = ml[e];
+      x[k] = po[e * (D / 4) + dq];
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) merge(v[k], x[k]);
+  }
+  for (; s <= s1; ++s) {
+    const size_t e = entry(s);
+    merge(ml[e], po[e * (D / 4) + dq]);
+  }
+  const f32x4 av = l > 0.0f ? o * (a.kv_scale / l) : f32x4{0.f, 0.f, 0.f, 0.f};
+  const float ms2 = row16_sum(av[0] * av[0] + av[1] * av[1] + av[2] * av[2] + av[3] * av[3]) *
+                    (1.0f / 64.0f);
+  const float rn = 1.0f / sqrtf(ms2 + a.eps);
+  const uint32_t gw[2] = {graw.x, graw.y};
+  uint32_t packed[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const float g0 = __uint_as_float(gw[k] << 16), g1 = __uint_as_float(gw[k] & 0xffff0000u);
+    const float y0 = av[2 * k] * rn * wo[2 * k] / (1.0f + expf(-g0));
+    const float y1 = av[2 * k + 1] * rn * wo[2 * k + 1] / (1.0f + expf(-g1));
+    packed[k] = (uint32_t)f32_to_bf16_bits(y0) | ((uint32_t)f32_to_bf16_bits(y1) << 16);
+  }
+  *reinterpret_cast<uint2 *>(a.out + (size_t)t * (HQ * D) + h * D + 4 * dq) =
+      uint2{packed[0], packed[1]};
+}
+
 void launch_combine(const StepArgs &a, hipStream_t stream) {
-  hipLaunchKernelGGL(combine_kernel, dim3(a.B * a.L * HQ), dim3(256), 0, stream, a);
+  if (a.L > 8)
+    hipLaunchKernelGGL(combine_tokens_kernel, dim3(a.B * a.L), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL(combine_kernel, dim3(a.B * a.L * HQ), dim3(256), 0, stream, a);
 }
 
 }  // namespace museattn

@@ -79,7 +79,7 @@ const char *museattn_strerror(int status) {
     case MUSEATTN_ERR_SHAPE:
       return "B, L, B * ceil(L / 16) (L > 8), max_seq_len or num_rows out of range";
     case MUSEATTN_ERR_TABLE: return "table_stride < ceil(max_seq_len / page_size)";
-    case MUSEATTN_ERR_ALIGN: return "misaligned pointer (caches need 16-byte alignment)";
+    case MUSEATTN_ERR_ALIGN: return "misaligned pointer (caches, qkv and weights need 16 bytes, out 8)";
     case MUSEATTN_ERR_WORKSPACE: return "workspace too small or not 256-byte aligned";
     case MUSEATTN_ERR_PARAM: return "kv_scale, eps, q_scale, rope_base or work_groups out of range";
     case MUSEATTN_ERR_ALIAS: return "out overlaps qkv";
@@ -114,10 +114,12 @@ int museattn_check_args(const void *qkv, const int32_t *positions, const int32_t
   if (num_rows < page_size || num_rows % page_size != 0 || num_rows > (int64_t(1) << 32))
     return MUSEATTN_ERR_SHAPE;
   if ((int64_t)table_stride * page_size < max_seq_len || table_stride < 1) return MUSEATTN_ERR_TABLE;
-  if (!aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(qkv, 2) || !aligned(out, 2) ||
+  // the kernels read q, k, v and gate slices of 16 B, the norm weights as
+  // float4 and write 8-byte output pieces
+  if (!aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(qkv, 16) || !aligned(out, 8) ||
       !aligned(positions, 4) || !aligned(table, 4) || !aligned(seq_lens, 4) ||
-      !aligned(params->q_norm_w, 4) || !aligned(params->k_norm_w, 4) ||
-      !aligned(params->o_norm_w, 4))
+      !aligned(params->q_norm_w, 16) || !aligned(params->k_norm_w, 16) ||
+      !aligned(params->o_norm_w, 16))
     return MUSEATTN_ERR_ALIGN;
   if (!(std::isfinite(kv_scale) && kv_scale > 0.0f) ||
       !(std::isfinite(params->eps) && params->eps >= 0.0f) || !std::isfinite(params->q_scale) ||

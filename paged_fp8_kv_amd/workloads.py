@@ -95,6 +95,14 @@ class Workload:
             span = self.seq_lens.astype(np.int64) - lo
         return int(span.sum()) * 2 * ROW_BYTES
 
+    @property
+    def attn_flops(self) -> int:
+        """Algorithmic FLOPs of the attention: 4 * 64 per (visible key, token, head)
+        (q.k and p.v, a multiply and an add each)."""
+        p = self.positions.astype(np.int64)
+        keys = p + 1 if self.layer_kind == FULL else np.minimum(p + 1, 2048)
+        return int(keys.sum()) * HQ * D * 4
+
     def subset(self, requests) -> "Workload":
         """The same draws restricted to some requests (their pool placement kept)."""
         req = [int(b) for b in requests]
@@ -213,10 +221,25 @@ def config(cid: str, pool_rows: int | None = None) -> Workload:
     if cid == "4":
         return make("paged64-full-decode-b16-kvscale1/64", 1004, 16, 1, (60000, 100000), FULL,
                     64, 1.0 / 64, pool_rows)
+    # prefill blocks (the prefill task page's scored shapes; seed 1100 + index)
+    prefill = {
+        "pf1f": ("prefill-turn1-full-ctx80k-L753", 1, 80000, 753, FULL),
+        "pf1s": ("prefill-turn1-sliding-ctx80k-L753", 1, 80000, 753, SLIDING),
+        "pf4f": ("prefill-turn4-full-b4-ctx80k-L753", 4, 80000, 753, FULL),
+        "pf4s": ("prefill-turn4-sliding-b4-ctx80k-L753", 4, 80000, 753, SLIDING),
+        "pff0": ("prefill-first-full-ctx0-L16384", 1, 0, 16384, FULL),
+        "pfs32": ("prefill-first-sliding-ctx32k-L16384", 1, 32768, 16384, SLIDING),
+        "pff32": ("prefill-first-full-ctx32k-L16384", 1, 32768, 16384, FULL),
+        "pff64": ("prefill-first-full-ctx64k-L16384", 1, 65536, 16384, FULL),
+    }
+    if cid in prefill:
+        name, B, ctx, L, kind = prefill[cid]
+        return make(name, 1100 + list(prefill).index(cid), B, L, ctx, kind, 1, 1.0, pool_rows)
     raise KeyError(cid)
 
 
 CONFIG_IDS = ("0", "1", "2", "3s", "3f", "4")
+PREFILL_IDS = ("pf1f", "pf1s", "pf4f", "pf4s", "pff0", "pfs32", "pff32", "pff64")
 
 
 # --------------------------------------------------------------------------

@@ -89,6 +89,8 @@ def test_valid_arguments_pass():
     (dict(page_size=64, table_stride=15, num_rows=6400), -5),
     (dict(kc=A["kc"] + 8), -6),
     (dict(qkv=A["qkv"] + 1), -6),
+    (dict(qkv=A["qkv"] + 8), -6),     # q, k, v and gate are read in 16-byte pieces
+    (dict(out=A["out"] + 4), -6),     # the output is written in 8-byte pieces
     (dict(ws_bytes=1024), -7),
     (dict(ws=A["ws"] + 128), -7),
     (dict(kv_scale=0.0), -8),
