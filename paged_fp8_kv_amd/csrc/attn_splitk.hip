@@ -198,151 +198,215 @@ __device__ __forceinline__ void compute_chunk(const RowBuf &rb, int u0, int lane
   }
 }
 
-// Verify blocks (L >= 2): a dense contraction per KV head.  The 64 columns of
-// Q_g^T are (token, head) pairs, column tile ct = tokens 2ct and 2ct + 1 x the
-// group's 8 heads (lane column n = token 2ct + n/8, head 8g + n%8).  Wave w
-// works on KV head g = w % 2, column tiles 2h and 2h + 1 of half h = (w/2) % 2,
-// and every other chunk starting at w / 4.  Per 32-key chunk:
-//  * K_g rows: lane (n, j) loads 16 B at byte 64g + 16j of key 16t + n (key
-//    tile t); K-step kk takes its half kk, dims 16j + 8kk + i, as for decode;
-//  * S^T (32 keys x 64 columns) = 2 key tiles x 4 column tiles x 2 K-steps,
-//    q as bf16 hi + lo;
-//  * V_g^T: lane (n, j) loads 4 B (dims 4n..4n+3 of KV head g) of the 8 keys
-//    it holds P for; a 4x4 byte transpose of each 4 keys turns them into 4
-//    M-tiles, M-tile dt row n = dim 4n + dt, so O^T tile (dt, ct) row 4j + r
-//    is dim 16j + 4r + dt;
-//  * the online softmax runs per column exactly as for decode.
-struct RowBuf2 {
-  uint4 k[2];      // key tile t: 16 B of KV head g's half row
-  uint32_t v[8];   // 4 B of V rows of the 8 keys this lane holds P for
+// Verify and prefill blocks (L >= 2): per KV head g, a dense contraction of
+// the block's (token, head) columns with the keys.  Column tile ct holds
+// tokens 2ct and 2ct + 1 of the unit (lane column n: token 2ct + n/8, head
+// 8g + n%8).  The work-group moves through a segment in steps of 64 keys (two
+// 32-key sub-chunks) that its 8 waves share:
+//  * staging: thread t loads 32 B of key t/8's K row (t%8 < 4) or V row
+//    (t%8 >= 4), so 4 lanes read one whole 128-B row; the bytes are converted
+//    to bf16 once for the work-group and written, key-major, into one of two
+//    LDS stage buffers (rows padded against bank conflicts).  The loads run
+//    BLOCK_PREFETCH steps ahead in registers; one barrier per step.
+//  * S^T (32 keys x 16 columns) per sub-chunk and column tile: 2 key tiles x
+//    2 K-steps of v_mfma_f32_16x16x32_bf16; A = K rows from LDS (K-step kk:
+//    dims 32kk + 8j..+7 in lane (n, j)), B = Q^T from registers as bf16 hi +
+//    lo, so the product keeps ~16 significant bits of q.
+//  * S^T leaves column n's scores for keys 4j..4j+3 (key tile 0) and
+//    16+4j..16+4j+3 (key tile 1) in lane (n, j): the B operand layout of
+//    O^T = V^T . P^T, so P stays in place, rounded to bf16.
+//  * V^T tiles come from the row-major stage through the gfx950 transposing
+//    LDS read (ds_read_b64_tr_b16): within a 16-lane group, lane s names 4
+//    dims of key k0 + s/4 and lane i receives dim i of those 4 keys.
+//  * online softmax in base 2 with decode's lazy reference max.
+// Verify (L <= 8, up to 4 column tiles): wave w takes KV head w % 2, column
+// tiles 2h and 2h + 1 with h = (w / 2) % 2, and sub-chunk w / 4 of each step;
+// the two sub-chunk halves merge in LDS.  Prefill (token groups of 16, 8
+// column tiles per KV head): wave w takes KV head w % 2, column tiles 2(w/2)
+// and 2(w/2) + 1, and both sub-chunks of each step.
+constexpr int STAGE_KEYS = 64;
+constexpr int KROW = 272;   // LDS bytes per key of the K stage: 2 heads x 64 bf16, + 16
+constexpr int VROW = 288;   // of the V stage: + 32 (a transposing read spans 4 rows x 32 B)
+
+struct Stage {
+  uint8_t k[STAGE_KEYS * KROW];
+  uint8_t v[STAGE_KEYS * VROW];
 };
 
-struct VerifyState {
-  f32x4 o[4][2];   // [dim tile][column tile of the wave's half]
-  float m[2], l[2];
-  int lo[2], hi[2];   // visible key range of the lane's column's token
+struct BlockState {
+  // O^T [dim tile dt][column tile c]: element r of lane (n, j) = dim 16dt + 4j + r.
+  // Tile 4 is ones . P^T: every element holds the column's running sum of P.
+  f32x4 o[5][2];
+  f32x4 negm[2];   // -m (0 while m = -inf), the accumulator the scores start from
+  float m[2];      // the column's reference max (log2 units)
+  int lo[2], hi[2];   // visible key range of the lane column's token, inclusive
 };
 
-// Q_g^T operands of one KV head in LDS, shared by that head's 4 waves:
-// [column tile][K-step][hi, lo][lane].
-struct VerifyQ {
-  bf16x8 op[4][2][2][64];
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// One step's staged bytes between their load and their LDS store.
+struct StageIn {
+  uint4 x[2];
 };
 
-__device__ __forceinline__ void load_rows2(RowBuf2 &rb, const uint8_t *__restrict__ kc,
-                                           const uint8_t *__restrict__ vc, const uint32_t *lrows,
-                                           int n, int j, int g) {
-  const uint32_t k0 = lrows[n];
-  const uint32_t k1 = lrows[16 + n];
-  const uint4 va = *reinterpret_cast<const uint4 *>(lrows + 4 * j);
-  const uint4 vb = *reinterpret_cast<const uint4 *>(lrows + 16 + 4 * j);
-  rb.k[0] = *reinterpret_cast<const uint4 *>(kc + (uint64_t)k0 * ROW + 64 * g + 16 * j);
-  rb.k[1] = *reinterpret_cast<const uint4 *>(kc + (uint64_t)k1 * ROW + 64 * g + 16 * j);
-  const uint32_t vr[8] = {va.x, va.y, va.z, va.w, vb.x, vb.y, vb.z, vb.w};
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-    rb.v[i] = *reinterpret_cast<const uint32_t *>(vc + (uint64_t)vr[i] * ROW + 64 * g + 4 * n);
-}
-
-// The chunk's K_g and V_g^T operands (fp8 -> bf16 is exact).
-struct ChunkOps2 {
-  bf16x8 ka[2][2];   // [key tile][K-step]
-  bf16x8 va[4];      // [dim tile]
+// Which 32 bytes thread t stages: wave w takes keys 8w..8w+7 of the step.
+// Lanes 0-31 take K rows (key 8w + l%8, part [0, 2, 1, 3][l/8]); lanes 32-63
+// take V rows, each group of 8 lanes 4 keys x 2 adjacent parts.  A part is 32
+// fp8 bytes = 64 bf16 bytes = 4 chunks of 16 B, written one chunk per
+// ds_write_b128.  In the V stage an odd part's chunk q sits at slot (q - 1) %
+// 4; with this order the 8 (or 16) lanes an LDS pass serves hit distinct
+// banks, for stores as well as for the operand reads.
+struct StageMap {
+  int key, part;
+  bool v;
 };
 
-__device__ __forceinline__ ChunkOps2 chunk_ops2(const RowBuf2 &rb) {
-  ChunkOps2 op;
-#pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    op.ka[t][0] = fp8x8_to_bf16(rb.k[t].x, rb.k[t].y);
-    op.ka[t][1] = fp8x8_to_bf16(rb.k[t].z, rb.k[t].w);
+__device__ __forceinline__ StageMap stage_map(int t) {
+  const int w = t >> 6, l = t & 63;
+  StageMap m;
+  if (l < 32) {
+    const int gq = l >> 3;
+    m = StageMap{8 * w + (l & 7), 2 * (gq & 1) + (gq >> 1), false};
+  } else {
+    const int l2 = l - 32, grp = l2 >> 3;
+    m = StageMap{8 * w + ((l2 & 7) >> 1) + 4 * (grp & 1), 2 * (grp >> 1) + (l2 & 1), true};
   }
-  uint32_t ty[4], tz[4];
-  transpose4x4(rb.v[0], rb.v[1], rb.v[2], rb.v[3], ty[0], ty[1], ty[2], ty[3]);
-  transpose4x4(rb.v[4], rb.v[5], rb.v[6], rb.v[7], tz[0], tz[1], tz[2], tz[3]);
-#pragma unroll
-  for (int dt = 0; dt < 4; ++dt) op.va[dt] = fp8x8_to_bf16(ty[dt], tz[dt]);
-  return op;
+  return m;
 }
 
-// One column tile of one chunk: S^T (32 keys x 16 columns) from the tile's
-// Q^T operands (K-steps 0, 1; hi and lo), mask, online softmax of the
-// columns, and O^T += V^T . P^T into state slot c.
-__device__ __forceinline__ void tile_step(const ChunkOps2 &op, bf16x8 qh0, bf16x8 ql0, bf16x8 qh1,
-                                          bf16x8 ql1, int u0, int j, VerifyState &st, int c) {
-  f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-  s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op.ka[0][0], qh0, s0, 0, 0, 0);
-  s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op.ka[1][0], qh0, s1, 0, 0, 0);
-  s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op.ka[0][0], ql0, s0, 0, 0, 0);
-  s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op.ka[1][0], ql0, s1, 0, 0, 0);
-  s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op.ka[0][1], qh1, s0, 0, 0, 0);
-  s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op.ka[1][1], qh1, s1, 0, 0, 0);
-  s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op.ka[0][1], ql1, s0, 0, 0, 0);
-  s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op.ka[1][1], ql1, s1, 0, 0, 0);
+__device__ __forceinline__ void stage_load(const StepArgs &a, const uint32_t *lrows, int key0,
+                                           StageIn &in) {
+  const StageMap m = stage_map(threadIdx.x);
+  int kk = key0 + m.key;
+  kk = kk < MAX_SPLIT_LDS - 1 ? kk : MAX_SPLIT_LDS - 1;
+  const uint8_t *src = (m.v ? a.v_cache : a.k_cache) + (uint64_t)lrows[kk] * ROW + m.part * 32;
+  in.x[0] = *reinterpret_cast<const uint4 *>(src);
+  in.x[1] = *reinterpret_cast<const uint4 *>(src + 16);
+}
+
+// Slot of chunk q of a V part: odd parts rotate by one.
+__device__ __forceinline__ int v_slot(int part, int q) { return (q - (part & 1)) & 3; }
+
+__device__ __forceinline__ void stage_store(const StageIn &in, Stage &st) {
+  const StageMap m = stage_map(threadIdx.x);
+  uint8_t *dst = m.v ? st.v + m.key * VROW + m.part * 64 : st.k + m.key * KROW + m.part * 64;
+  const bf16x8 c[4] = {fp8x8_to_bf16(in.x[0].x, in.x[0].y), fp8x8_to_bf16(in.x[0].z, in.x[0].w),
+                       fp8x8_to_bf16(in.x[1].x, in.x[1].y), fp8x8_to_bf16(in.x[1].z, in.x[1].w)};
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    *reinterpret_cast<bf16x8 *>(dst + 16 * (m.v ? v_slot(m.part, q) : q)) = c[q];
+}
+
+// A operand of S^T: key tile t of sub-chunk sc, K-step kk, KV head g.
+__device__ __forceinline__ bf16x8 k_operand(const Stage &st, int sc, int t, int kk, int n, int j,
+                                            int g) {
+  return *reinterpret_cast<const bf16x8 *>(st.k + (32 * sc + 16 * t + n) * KROW + g * 128 +
+                                           kk * 64 + j * 16);
+}
+
+// A operand of O^T = V^T . P^T: dim tile dt of sub-chunk sc, KV head g.  Lane
+// (n, j) receives dim 16dt + n of keys 4j..4j+3 (elements 0-3) and
+// 16+4j..16+4j+3 (elements 4-7), the keys whose P it holds.
+__device__ __forceinline__ bf16x8 v_operand(const Stage &st, int sc, int dt, int n, int j, int g) {
+  // dims 16dt + 4(n%4).. of head g: part 2g + dt/2, chunk 2(dt%2) + (n%4)/2, 8 B in
+  const int part = 2 * g + (dt >> 1), q = 2 * (dt & 1) + ((n & 3) >> 1);
+  const uint8_t *p = st.v + (32 * sc + 4 * j + (n >> 2)) * VROW + part * 64 + 16 * v_slot(part, q) +
+                     8 * (n & 1);
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)p);
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p + 16 * VROW));
+  typedef short i16x8 __attribute__((ext_vector_type(8)));
+  const i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// IEEE maximum (gfx950 v_maximum3_f32; no operand canonicalisation needed).
+__device__ __forceinline__ float fmax_ieee(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
+// Mask, online softmax and O^T += V^T . P^T for column tile c of one
+// sub-chunk whose first key is u0.  s0, s1: the two key tiles of S^T, already
+// relative to the reference max (the products start from -m), or raw while
+// the column has no reference yet.
+__device__ __forceinline__ void block_tile(f32x4 s0, f32x4 s1, const bf16x8 (&va)[4], bf16x8 ones,
+                                           int u0, int j, BlockState &st, int c) {
   float sc[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
   const int lo = st.lo[c], hi = st.hi[c];
   if (u0 < lo || u0 + CHUNK - 1 > hi) {
+    // score i is key u0 + 4j + off_i, off_i = 16 (i / 4) + i % 4
+    const int elo = lo - u0 - 4 * j, ehi = hi - u0 - 4 * j;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int u = u0 + (i >> 2) * 16 + 4 * j + (i & 3);
-      if (u < lo || u > hi) sc[i] = -INFINITY;
+      const int off = (i >> 2) * 16 + (i & 3);
+      if (off < elo || off > ehi) sc[i] = -INFINITY;
     }
   }
-  float cmax = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
-                     fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
-  cmax = head_max(cmax);
-  if (__any(cmax > st.m[c] + RESCALE_SLACK)) {
-    const float mnew = fmaxf(st.m[c], cmax);
-    const float alpha = mnew == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(st.m[c] - mnew);
-    st.l[c] *= alpha;
+  const float lmax = fmax_ieee(fmax_ieee(fmax_ieee(sc[0], sc[1]), fmax_ieee(sc[2], sc[3])),
+                               fmax_ieee(fmax_ieee(sc[4], sc[5]), fmax_ieee(sc[6], sc[7])));
+  // Lazy reference max: it moves only when a score passes it by more than
+  // RESCALE_SLACK (so P <= 2^SLACK), or for the column's first visible keys.
+  const bool fresh = st.m[c] == -INFINITY;
+  if (__any(lmax > RESCALE_SLACK || (fresh && lmax != -INFINITY))) {
+    const float cm = head_max(lmax);   // the column's max, relative (or raw if fresh)
+    float d, alpha;
+    if (fresh) {
+      d = cm == -INFINITY ? 0.0f : cm;
+      alpha = 1.0f;
+      st.m[c] = cm;
+    } else {
+      d = fmaxf(cm, 0.0f);
+      alpha = __builtin_amdgcn_exp2f(-d);
+      st.m[c] += d;
+    }
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) st.o[dt][c] *= alpha;
-    st.m[c] = mnew;
+    for (int i = 0; i < 8; ++i) sc[i] -= d;
+#pragma unroll
+    for (int dt = 0; dt < 5; ++dt) st.o[dt][c] *= alpha;
+    const float nm = st.m[c] == -INFINITY ? 0.0f : -st.m[c];
+    st.negm[c] = f32x4{nm, nm, nm, nm};
   }
-  const float muse = st.m[c] == -INFINITY ? 0.0f : st.m[c];
   float pv[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    pv[i] = __builtin_amdgcn_exp2f(sc[i] - muse);
-    st.l[c] += pv[i];
-  }
-  bf16x8 ph, pl;
+  for (int i = 0; i < 8; ++i) pv[i] = __builtin_amdgcn_exp2f(sc[i]);
+  bf16x8 ph;
 #pragma unroll
   for (int i = 0; i < 8; i += 2) {
-    const f32x2 f = {pv[i], pv[i + 1]};
-    const bf16x2 h = __builtin_convertvector(f, bf16x2);
-    const bf16x2 r = __builtin_convertvector(f - __builtin_convertvector(h, f32x2), bf16x2);
-    ph[i] = h[0]; ph[i + 1] = h[1];
-    pl[i] = r[0]; pl[i + 1] = r[1];
+    const bf16x2 h = __builtin_convertvector((f32x2{pv[i], pv[i + 1]}), bf16x2);
+    ph[i] = h[0];
+    ph[i + 1] = h[1];
   }
 #pragma unroll
-  for (int dt = 0; dt < 4; ++dt) {
-    st.o[dt][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op.va[dt], ph, st.o[dt][c], 0, 0, 0);
-    st.o[dt][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op.va[dt], pl, st.o[dt][c], 0, 0, 0);
-  }
+  for (int dt = 0; dt < 4; ++dt)
+    st.o[dt][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[dt], ph, st.o[dt][c], 0, 0, 0);
+  st.o[4][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, ph, st.o[4][c], 0, 0, 0);
 }
 
-// Verify: the wave's two column tiles (2 half, 2 half + 1), Q^T from LDS.
-__device__ __forceinline__ void compute_chunk2(const RowBuf2 &rb, int u0, int lane, int half,
-                                               int nct, VerifyState &st, const VerifyQ &q) {
-  const ChunkOps2 op = chunk_ops2(rb);
+// One sub-chunk (32 keys from u0) for the wave's nc live column tiles.
+__device__ __forceinline__ void block_subchunk(const Stage &stg, int sc, int u0, int lane, int g,
+                                               int nc, const bf16x8 (&qh)[2][2],
+                                               const bf16x8 (&ql)[2][2], BlockState &st) {
+  const int n = lane & 15, j = lane >> 4;
+  bf16x8 ka[2][2], va[4];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) ka[t][kk] = k_operand(stg, sc, t, kk, n, j, g);
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) va[dt] = v_operand(stg, sc, dt, n, j, g);
+  const __bf16 one = (__bf16)1.0f;
+  const bf16x8 ones = {one, one, one, one, one, one, one, one};
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
-    const int ct = 2 * half + c;
-    if (ct >= nct) break;   // uniform
-    tile_step(op, q.op[ct][0][0][lane], q.op[ct][0][1][lane], q.op[ct][1][0][lane],
-              q.op[ct][1][1][lane], u0, lane >> 4, st, c);
-  }
-}
-
-// Prefill: the wave's two column tiles, Q^T in registers ([tile][K-step]).
-__device__ __forceinline__ void compute_chunk_prefill(const RowBuf2 &rb, int u0, int lane,
-                                                      const bf16x8 (&qh)[2][2],
-                                                      const bf16x8 (&ql)[2][2], VerifyState &st) {
-  const ChunkOps2 op = chunk_ops2(rb);
+    if (c >= nc) break;   // uniform
+    f32x4 s0 = st.negm[c], s1 = st.negm[c];
 #pragma unroll
-  for (int c = 0; c < 2; ++c)
-    tile_step(op, qh[c][0], ql[c][0], qh[c][1], ql[c][1], u0, lane >> 4, st, c);
+    for (int kk = 0; kk < 2; ++kk) {
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[0][kk], qh[c][kk], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[1][kk], qh[c][kk], s1, 0, 0, 0);
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[0][kk], ql[c][kk], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[1][kk], ql[c][kk], s1, 0, 0, 0);
+    }
+    block_tile(s0, s1, va, ones, u0, j, st, c);
+  }
 }
 
 // Split and QK-norm of one (token, head) query and RoPE on sliding layers
@@ -479,9 +543,6 @@ __device__ __forceinline__ void write_new_rows(const StepArgs &a, int b, unsigne
 #ifndef MUSEATTN_DECODE_NBUF
 #define MUSEATTN_DECODE_NBUF 2
 #endif
-#ifndef MUSEATTN_VERIFY_NBUF
-#define MUSEATTN_VERIFY_NBUF 2
-#endif
 
 constexpr int PIECE_CHUNKS = MAX_SPLIT_LDS / CHUNK;   // chunks whose rows one LDS fill holds
 
@@ -527,7 +588,7 @@ struct Lds {
   union {
     float sm_o[WAVES][HQ][D];   // decode: the 8 waves' O per head
     float mrg[2][64][68];       // verify merge: chunk lane 1's O per KV head and column (padded)
-    VerifyQ vq[2];              // verify chunk loop: Q^T operands per KV head
+    Stage stg[MODE == 0 ? 1 : 2];   // verify and prefill: the K/V stage buffers
   };
   float mrg_ml[2][64][2];       // verify merge: its (max, sum) per column
   QOps dq;                      // decode: the token's Q^T operands
@@ -539,24 +600,18 @@ struct Lds {
   int req_p0[MAXU];          // position of each unit's first token (sliding layers)
 };
 
-// One segment: chunks [x, y) of request b's key range (chunk i = keys
+// One decode segment: chunks [x, y) of request b's key range (chunk i = keys
 // kbase + 32i ..), processed by the whole work-group, leaving one partial per
-// (token, head) in slot `slot`.  MODE 0: decode (L = 1), the 8 waves take
-// interleaved chunks and both KV heads.  MODE 2: verify (L >= 2), wave w takes
-// KV head w % 2, column half (w / 2) % 2 and every other chunk from w / 4.
-template <int MODE, int NBUF>
+// head in slot `slot`.  The 8 waves take interleaved chunks and both KV heads.
+template <int NBUF>
 __device__ __forceinline__ void process_segment(const StepArgs &a, int b, const KeyRange &r, int x,
-                                                int y, int slot, Lds<MODE> &sh) {
+                                                int y, int slot, Lds<0> &sh) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int n = lane & 15, j = lane >> 4;
   const float qmul = a.kv_scale * (LOG2E / 8.0f);
   const int nseg = y - x;
   const int npieces = (nseg + PIECE_CHUNKS - 1) / PIECE_CHUNKS;
   auto piece_x = [&](int pc) { return x + (int)((int64_t)pc * nseg / npieces); };
-  const int g = wave & 1;                  // verify: the wave's KV head,
-  const int half = (wave >> 1) & 1;        // column half (column tiles 2 half, 2 half + 1)
-  const int cl = wave >> 2;                // and chunk lane
-  const int nct = (a.L + 1) >> 1;          // verify: live column tiles
 
   // One batch of loads for everything the segment starts with: positions, the
   // first piece's table entries, the tokens' q rows and norm weights, and the
@@ -564,19 +619,9 @@ __device__ __forceinline__ void process_segment(const StepArgs &a, int b, const 
   int pos[8];
 #pragma unroll
   for (int jt = 0; jt < 8; ++jt) pos[jt] = a.positions[b * a.L + (jt < a.L ? jt : a.L - 1)];
-  int cpos[2];   // verify: position of the token of the lane's column, per column tile
-#pragma unroll
-  for (int c = 0; c < 2; ++c) {
-    const int tk = 2 * (2 * half + c) + (n >> 3);
-    cpos[c] = MODE == 0 ? 0 : a.positions[b * a.L + (tk < a.L ? tk : a.L - 1)];
-  }
   TableIn tin;
   load_table_in(a, b, r, r.kbase + x * CHUNK, tin);
-  // decode: head n of the token; verify: column tile 2 half + cl of KV head g
-  const int qct = 2 * half + cl;
-  const int qtk = MODE == 0 ? 0 : 2 * qct + (n >> 3);
-  const QIn qin = load_q_in(a, b * a.L + (qtk < a.L ? qtk : a.L - 1),
-                            MODE == 0 ? n : 8 * g + (n & 7), j);
+  const QIn qin = load_q_in(a, b * a.L, n, j);   // head n of the token
   const f32x4 *w4 = reinterpret_cast<const f32x4 *>(a.wq + 16 * j);
   const f32x4 wv[4] = {w4[0], w4[1], w4[2], w4[3]};
   const RowIn rin = load_row_in(a, b);
@@ -596,36 +641,12 @@ __device__ __forceinline__ void process_segment(const StepArgs &a, int b, const 
     lo = a.sliding ? p - (WINDOW - 1) : 0;
   };
   TokState ts;
-  VerifyState vs;
-  if constexpr (MODE == 0) {
-    token_range(true, pos[0], ts.lo, ts.hi);
-    ts.m = -INFINITY;
-    ts.l = 0.0f;
+  token_range(true, pos[0], ts.lo, ts.hi);
+  ts.m = -INFINITY;
+  ts.l = 0.0f;
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt) ts.o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (wave == 0) make_q(a, qin, wv, lane, qmul, sh.cs[0], sh.dq);   // published by the barrier below
-  } else {
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      token_range(2 * (2 * half + c) + (n >> 3) < a.L, cpos[c], vs.lo[c], vs.hi[c]);
-      vs.m[c] = -INFINITY;
-      vs.l[c] = 0.0f;
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt) vs.o[dt][c] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-    const int ct = qct;
-    if (ct < nct) {   // uniform
-      float yq[16];
-      q_values(a, qin, wv, j, sh.cs[qtk < a.L ? qtk : a.L - 1], yq);
-      bf16x8 h0, l0, h1, l1;
-      pack_q(yq, 0, qmul, h0, l0);
-      pack_q(yq, 1, qmul, h1, l1);
-      sh.vq[g].op[ct][0][0][lane] = h0;
-      sh.vq[g].op[ct][0][1][lane] = l0;
-      sh.vq[g].op[ct][1][0][lane] = h1;
-      sh.vq[g].op[ct][1][1][lane] = l1;
-    }
-  }
+  for (int mt = 0; mt < 8; ++mt) ts.o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (wave == 0) make_q(a, qin, wv, lane, qmul, sh.cs[0], sh.dq);   // published by the barrier below
   // New rows of the block tokens whose key falls in this segment: only this
   // work-group reads them, so a workgroup release before the barrier orders
   // the writes before its own loads.
@@ -658,233 +679,211 @@ __device__ __forceinline__ void process_segment(const StepArgs &a, int b, const 
     // the steady state every load is unconditional -- chunk indices past the
     // end are clamped to the last chunk -- so the compiler can count the loads
     // in flight and wait only for the buffer it is about to use.
-    const int c0 = MODE == 0 ? wave : cl;
-    const int cstep = MODE == 0 ? WAVES : 2;
+    const int c0 = wave;
+    const int cstep = WAVES;
     const int nloc = nchunks > c0 ? (nchunks - c0 + cstep - 1) / cstep : 0;
     if (nloc > 0) {
       const int last = nloc - 1;
       auto rows_of = [&](int i) { return sh.lrows + (c0 + i * cstep) * CHUNK; };
       auto key_of = [&](int i) { return kstart + (c0 + i * cstep) * CHUNK; };
-      if constexpr (MODE == 0) {
-        RowBuf buf[NBUF];
+      RowBuf buf[NBUF];
 #pragma unroll
-        for (int k = 0; k < NBUF; ++k)
-          load_rows(buf[k], a.k_cache, a.v_cache, rows_of(k < last ? k : last), n, j);
-        int i = 0;
-        for (; i + NBUF <= nloc; i += NBUF) {
+      for (int k = 0; k < NBUF; ++k)
+        load_rows(buf[k], a.k_cache, a.v_cache, rows_of(k < last ? k : last), n, j);
+      int i = 0;
+      for (; i + NBUF <= nloc; i += NBUF) {
 #pragma unroll
-          for (int k = 0; k < NBUF; ++k) {
-            compute_chunk(buf[k], key_of(i + k), lane, ts, sh.dq);
-            const int inext = i + k + NBUF;
-            load_rows(buf[k], a.k_cache, a.v_cache, rows_of(inext < last ? inext : last), n, j);
-          }
+        for (int k = 0; k < NBUF; ++k) {
+          compute_chunk(buf[k], key_of(i + k), lane, ts, sh.dq);
+          const int inext = i + k + NBUF;
+          load_rows(buf[k], a.k_cache, a.v_cache, rows_of(inext < last ? inext : last), n, j);
         }
-#pragma unroll
-        for (int k = 0; k < NBUF - 1; ++k)
-          if (i + k < nloc) compute_chunk(buf[k], key_of(i + k), lane, ts, sh.dq);
-      } else {
-        RowBuf2 buf[NBUF];
-#pragma unroll
-        for (int k = 0; k < NBUF; ++k)
-          load_rows2(buf[k], a.k_cache, a.v_cache, rows_of(k < last ? k : last), n, j, g);
-        int i = 0;
-        for (; i + NBUF <= nloc; i += NBUF) {
-#pragma unroll
-          for (int k = 0; k < NBUF; ++k) {
-            compute_chunk2(buf[k], key_of(i + k), lane, half, nct, vs, sh.vq[g]);
-            const int inext = i + k + NBUF;
-            load_rows2(buf[k], a.k_cache, a.v_cache, rows_of(inext < last ? inext : last), n, j, g);
-          }
-        }
-#pragma unroll
-        for (int k = 0; k < NBUF - 1; ++k)
-          if (i + k < nloc) compute_chunk2(buf[k], key_of(i + k), lane, half, nct, vs, sh.vq[g]);
       }
+#pragma unroll
+      for (int k = 0; k < NBUF - 1; ++k)
+        if (i + k < nloc) compute_chunk(buf[k], key_of(i + k), lane, ts, sh.dq);
     }
   }
 
-  if constexpr (MODE == 0) {
-    // Lane (n, j) holds O^T of head n at V-row bytes 8(4j + r) + mt, r < 4: KV
-    // head j/2, dims 32(j%2) + 8r + mt.  Only lanes whose KV head is head n's
-    // own hold meaningful values.
-    const bool own = (j >> 1) == (n >> 3);
-    const int dbase = 32 * (j & 1);
-    const float lsum = head_sum(ts.l);
-    if (j == 0) {
-      sh.sm_m[wave][n] = ts.m;
-      sh.sm_l[wave][n] = lsum;
+  // Lane (n, j) holds O^T of head n at V-row bytes 8(4j + r) + mt, r < 4: KV
+  // head j/2, dims 32(j%2) + 8r + mt.  Only lanes whose KV head is head n's
+  // own hold meaningful values.
+  const bool own = (j >> 1) == (n >> 3);
+  const int dbase = 32 * (j & 1);
+  const float lsum = head_sum(ts.l);
+  if (j == 0) {
+    sh.sm_m[wave][n] = ts.m;
+    sh.sm_l[wave][n] = lsum;
+  }
+  if (own) {
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      float *dst = &sh.sm_o[wave][n][dbase + 8 * rr];
+      *reinterpret_cast<f32x4 *>(dst) =
+          f32x4{ts.o[0][rr], ts.o[1][rr], ts.o[2][rr], ts.o[3][rr]};
+      *reinterpret_cast<f32x4 *>(dst + 4) =
+          f32x4{ts.o[4][rr], ts.o[5][rr], ts.o[6][rr], ts.o[7][rr]};
     }
-    if (own) {
+  }
+  __syncthreads();
+  // merge the waves: thread -> (head h, dims d2, d2 + 1)
+  const int h = tid >> 5, d2 = (tid & 31) * 2;
+  float M = -INFINITY;
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        float *dst = &sh.sm_o[wave][n][dbase + 8 * rr];
-        *reinterpret_cast<f32x4 *>(dst) =
-            f32x4{ts.o[0][rr], ts.o[1][rr], ts.o[2][rr], ts.o[3][rr]};
-        *reinterpret_cast<f32x4 *>(dst + 4) =
-            f32x4{ts.o[4][rr], ts.o[5][rr], ts.o[6][rr], ts.o[7][rr]};
-      }
+  for (int w = 0; w < WAVES; ++w) M = fmaxf(M, sh.sm_m[w][h]);
+  f32x2 o = {0.f, 0.f};
+  float lt = 0.0f;
+  if (M != -INFINITY) {
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) {
+      const float sc = __builtin_amdgcn_exp2f(sh.sm_m[w][h] - M);
+      lt += sc * sh.sm_l[w][h];
+      o += sc * *reinterpret_cast<const f32x2 *>(&sh.sm_o[w][h][d2]);
     }
-    __syncthreads();
-    // merge the waves: thread -> (head h, dims d2, d2 + 1)
-    const int h = tid >> 5, d2 = (tid & 31) * 2;
-    float M = -INFINITY;
+  }
+  const size_t e = (size_t)slot * HQ + h;   // L = 1
+  *reinterpret_cast<f32x2 *>(a.part_o + e * D + d2) = o;
+  if ((tid & 31) == 0) {
+    a.part_ml[e * 2] = M;
+    a.part_ml[e * 2 + 1] = lt;
+  }
+}
+
+// Blocks: the q of one (token, head) column in the lane layout of the block
+// path -- lane (n, j) holds dims 8j..8j+7 (K-step 0) and 32+8j..32+8j+7
+// (K-step 1) -- normed over the head's 4 lanes and, on sliding layers,
+// rotated (each RoPE pair (i, i+32) sits in one lane); cs: the token's 32
+// (cos, sin) pairs in LDS.
+struct QIn2 {
+  uint4 lo, hi;   // bf16 dims 8j..8j+7 and 32+8j..32+8j+7
+};
+
+__device__ __forceinline__ QIn2 load_q_in2(const StepArgs &a, int t, int head, int j) {
+  const uint16_t *src = a.qkv + (size_t)t * QKV_W + head * D + 8 * j;
+  return QIn2{*reinterpret_cast<const uint4 *>(src), *reinterpret_cast<const uint4 *>(src + 32)};
+}
+
+__device__ __forceinline__ void q_values2(const StepArgs &a, const QIn2 &in, const f32x4 (&wv)[4],
+                                          int j, const float2 *cs, float (&y)[16]) {
+  const uint32_t raw[8] = {in.lo.x, in.lo.y, in.lo.z, in.lo.w, in.hi.x, in.hi.y, in.hi.z, in.hi.w};
+  float x[16];
 #pragma unroll
-    for (int w = 0; w < WAVES; ++w) M = fmaxf(M, sh.sm_m[w][h]);
-    f32x2 o = {0.f, 0.f};
-    float lt = 0.0f;
-    if (M != -INFINITY) {
+  for (int k = 0; k < 8; ++k) {
+    x[2 * k] = __uint_as_float(raw[k] << 16);
+    x[2 * k + 1] = __uint_as_float(raw[k] & 0xffff0000u);
+  }
+  float ss = 0.0f;
 #pragma unroll
-      for (int w = 0; w < WAVES; ++w) {
-        const float sc = __builtin_amdgcn_exp2f(sh.sm_m[w][h] - M);
-        lt += sc * sh.sm_l[w][h];
-        o += sc * *reinterpret_cast<const f32x2 *>(&sh.sm_o[w][h][d2]);
-      }
-    }
-    const size_t e = (size_t)slot * HQ + h;   // L = 1
-    *reinterpret_cast<f32x2 *>(a.part_o + e * D + d2) = o;
-    if ((tid & 31) == 0) {
-      a.part_ml[e * 2] = M;
-      a.part_ml[e * 2 + 1] = lt;
-    }
-  } else {
-    // Merge chunk lane 1 into chunk lane 0 (a segment of one chunk leaves lane
-    // 1 empty).  Lane (n, j) of the wave's column tile ct holds column 16ct + n,
-    // dims 16j + 4r + dt in o[dt][c][r].
-    float lsum[2];
+  for (int k = 0; k < 16; ++k) ss += x[k] * x[k];
+  const float ms = head_sum(ss) * (1.0f / 64.0f);
+  const float den = sqrtf(ms + a.eps);
 #pragma unroll
-    for (int c = 0; c < 2; ++c) lsum[c] = head_sum(vs.l[c]);
-    if (nseg > 1) {   // uniform
-      __syncthreads();   // every wave is done with the Q^T operands (they share the buffer)
-      if (cl == 1) {
+  for (int k = 0; k < 16; ++k) y[k] = x[k] / den * wv[k >> 2][k & 3] * a.q_scale;
+  if (a.sliding) {
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          const int ct = 2 * half + c;
-          if (ct >= nct) break;
-          float *row = sh.mrg[g][16 * ct + n];
-#pragma unroll
-          for (int rr = 0; rr < 4; ++rr)
-            *reinterpret_cast<f32x4 *>(row + 16 * j + 4 * rr) =
-                f32x4{vs.o[0][c][rr], vs.o[1][c][rr], vs.o[2][c][rr], vs.o[3][c][rr]};
-          if (j == 0) {
-            sh.mrg_ml[g][16 * ct + n][0] = vs.m[c];
-            sh.mrg_ml[g][16 * ct + n][1] = lsum[c];
-          }
-        }
-      }
-      __syncthreads();
-      if (cl == 0) {
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          const int ct = 2 * half + c;
-          if (ct >= nct) break;
-          const float *row = sh.mrg[g][16 * ct + n];
-          const float m1 = sh.mrg_ml[g][16 * ct + n][0], l1 = sh.mrg_ml[g][16 * ct + n][1];
-          const float M = fmaxf(vs.m[c], m1);
-          const float c0 = vs.m[c] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(vs.m[c] - M);
-          const float c1 = m1 == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m1 - M);
-          lsum[c] = lsum[c] * c0 + l1 * c1;
-#pragma unroll
-          for (int rr = 0; rr < 4; ++rr) {
-            const f32x4 v = *reinterpret_cast<const f32x4 *>(row + 16 * j + 4 * rr);
-#pragma unroll
-            for (int dt = 0; dt < 4; ++dt) vs.o[dt][c][rr] = vs.o[dt][c][rr] * c0 + v[dt] * c1;
-          }
-          vs.m[c] = M;
-        }
-      }
-    }
-    if (cl == 0) {
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const int ct = 2 * half + c;
-        const int tk = 2 * ct + (n >> 3);
-        if (ct >= nct) break;
-        if (tk >= a.L) continue;
-        const size_t e = ((size_t)slot * a.L + tk) * HQ + 8 * g + (n & 7);
-        if (j == 0) {
-          a.part_ml[e * 2] = vs.m[c];
-          a.part_ml[e * 2 + 1] = lsum[c];
-        }
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr)
-          *reinterpret_cast<f32x4 *>(a.part_o + e * D + 16 * j + 4 * rr) =
-              f32x4{vs.o[0][c][rr], vs.o[1][c][rr], vs.o[2][c][rr], vs.o[3][c][rr]};
-      }
+    for (int i = 0; i < 8; ++i) {   // pair 8j + i: x_i c - x_{i+32} s, x_{i+32} c + x_i s
+      const float2 c = cs[8 * j + i];
+      const float lo = y[i], hi = y[8 + i];
+      y[i] = lo * c.x - hi * c.y;
+      y[8 + i] = hi * c.x + lo * c.y;
     }
   }
 }
 
-#ifndef MUSEATTN_PREFILL_NBUF
-#define MUSEATTN_PREFILL_NBUF 2
+#ifndef MUSEATTN_BLOCK_PREFETCH
+#define MUSEATTN_BLOCK_PREFETCH 3
 #endif
 
-// Prefill (L > 8): plan unit = token group blk of request b, block tokens
-// j0 = 16 blk .. j0 + nt - 1.  Wave w takes KV head g = w % 2 and the group's
-// tokens 4qq .. 4qq + 3, qq = w / 2: its column tiles c = 0, 1 hold tokens
-// 4qq + 2c and 4qq + 2c + 1 (lane column n: token 4qq + 2c + n/8, head
-// 8g + n%8), with Q^T in registers.  Every wave walks all chunks of the
-// segment; the four waves of a KV head read the same rows, which the caches
-// serve after the first, so HBM sees each row once per 16 tokens.  The new
-// k/v rows were written by the rows kernel before this kernel started.
-template <int NBUF>
-__device__ __forceinline__ void process_segment_prefill(const StepArgs &a, int b, int blk,
-                                                        const KeyRange &r, int x, int y,
-                                                        int slot, Lds<3> &sh) {
+// One segment of a verify (MODE 2) or prefill (MODE 3) block: chunks [x, y)
+// of unit (b, blk)'s key range, leaving one partial per (token, head) in slot
+// `slot`.
+template <int MODE>
+__device__ __forceinline__ void process_segment_block(const StepArgs &a, int b, int blk,
+                                                      const KeyRange &r, int x, int y, int slot,
+                                                      Lds<MODE> &sh) {
+  constexpr bool VERIFY = MODE == 2;
+  constexpr int NR = MUSEATTN_BLOCK_PREFETCH;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int n = lane & 15, j = lane >> 4;
   const float qmul = a.kv_scale * (LOG2E / 8.0f);
   const int nseg = y - x;
   const int npieces = (nseg + PIECE_CHUNKS - 1) / PIECE_CHUNKS;
   auto piece_x = [&](int pc) { return x + (int)((int64_t)pc * nseg / npieces); };
-  const int g = wave & 1, qq = wave >> 1;
-  const int j0 = blk * a.tb;
-  const int nt = a.L - j0 < a.tb ? a.L - j0 : a.tb;   // tokens in the group
-  auto tok = [&](int c) { return 4 * qq + 2 * c + (n >> 3); };   // the lane column's token
+  const int g = wave & 1;
+  const int cq = VERIFY ? (wave >> 1) & 1 : wave >> 1;   // column tiles 2cq, 2cq + 1
+  const int cl = VERIFY ? wave >> 2 : 0;                 // verify: the wave's sub-chunk
+  const int j0 = blk * a.tb;                             // the unit's first block token
+  const int nt = a.L - j0 < a.tb ? a.L - j0 : a.tb;      // tokens in the unit
+  int nc = (nt + 1) / 2 - 2 * cq;                        // the wave's live column tiles
+  nc = nc < 0 ? 0 : (nc > 2 ? 2 : nc);
+  auto tok = [&](int c) { return 4 * cq + 2 * c + (n >> 3); };   // unit token of the lane column
 
-  // One batch: the first piece's table entries, the lane's column tokens'
-  // positions and q rows, the q norm weights.
+  // One batch of loads: the first piece's table entries, the column tokens'
+  // positions and q, the q norm weights and (verify) the new rows' inputs.
   TableIn tin;
   load_table_in(a, b, r, r.kbase + x * CHUNK, tin);
   int cpos[2];
-  QIn qin[2];
+  QIn2 qin[2];
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
     const int tk = tok(c);
     const int t = b * a.L + j0 + (tk < nt ? tk : nt - 1);
     cpos[c] = a.positions[t];
-    qin[c] = load_q_in(a, t, 8 * g + (n & 7), j);
+    qin[c] = load_q_in2(a, t, 8 * g + (n & 7), j);
   }
-  const f32x4 *w4 = reinterpret_cast<const f32x4 *>(a.wq + 16 * j);
-  const f32x4 wv[4] = {w4[0], w4[1], w4[2], w4[3]};
+  const f32x4 *w4 = reinterpret_cast<const f32x4 *>(a.wq);
+  const f32x4 wv[4] = {w4[2 * j], w4[2 * j + 1], w4[8 + 2 * j], w4[8 + 2 * j + 1]};
+  int pos[8];
+  RowIn rin;
+  if constexpr (VERIFY) {
+#pragma unroll
+    for (int jt = 0; jt < 8; ++jt) pos[jt] = a.positions[b * a.L + (jt < a.L ? jt : a.L - 1)];
+    rin = load_row_in(a, b);
+  }
   __builtin_amdgcn_sched_barrier(0);
 
-  __syncthreads();   // the previous segment is done with sh.cs and sh.lrows
+  __syncthreads();   // the previous segment is done with sh.cs, sh.lrows and the stage buffers
   if (a.sliding) {
-    const int tk = tid >> 5;   // 512 threads: 16 tokens x 32 pairs
+    const int tk = tid >> 5;   // 512 threads: up to 16 tokens x 32 pairs
     if (tk < nt) sh.cs[tk][tid & 31] = rope_cs(a.positions[b * a.L + j0 + tk], tid & 31);
     __syncthreads();
   }
   store_table(a, tin, sh.lrows);
 
   bf16x8 qh[2][2], ql[2][2];
-  VerifyState vs;
+  BlockState st;
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
     const int tk = tok(c);
     float yq[16];
-    q_values(a, qin[c], wv, j, sh.cs[tk < nt ? tk : nt - 1], yq);
+    q_values2(a, qin[c], wv, j, sh.cs[tk < nt ? tk : nt - 1], yq);
     pack_q(yq, 0, qmul, qh[c][0], ql[c][0]);
     pack_q(yq, 1, qmul, qh[c][1], ql[c][1]);
     // causal bound: the token's position; window: 2047 keys before it
     const int p = cpos[c];
-    vs.hi[c] = tk < nt ? (p < r.khi ? p : r.khi) : -1;
-    vs.lo[c] = a.sliding ? p - (WINDOW - 1) : 0;
-    vs.m[c] = -INFINITY;
-    vs.l[c] = 0.0f;
+    st.hi[c] = tk < nt ? (p < r.khi ? p : r.khi) : -1;
+    st.lo[c] = a.sliding ? p - (WINDOW - 1) : 0;
+    st.m[c] = -INFINITY;
+    st.negm[c] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) vs.o[dt][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int dt = 0; dt < 5; ++dt) st.o[dt][c] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  __syncthreads();   // the first piece's row ids are in LDS
+  if constexpr (VERIFY) {
+    // New rows of the block tokens whose key falls in this segment: only this
+    // work-group reads them, so a workgroup release before the barrier orders
+    // the writes before its own loads.  (Prefill rows come from rows_kernel.)
+    unsigned owned = 0;
+#pragma unroll
+    for (int jt = 0; jt < 8; ++jt) {
+      const int p = pos[jt];
+      const bool in = jt < a.L && p >= r.klo && p <= r.khi &&
+                      (p - r.kbase) / CHUNK >= x && (p - r.kbase) / CHUNK < y;
+      owned |= in ? 1u << jt : 0u;
+    }
+    if (owned && wave < 4) write_new_rows(a, b, owned, pos, sh.cs, rin);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  }
+  __syncthreads();   // the row ids (and verify's new rows) are in place
 
   for (int pc = 0; pc < npieces; ++pc) {
     const int px = piece_x(pc), py = piece_x(pc + 1);
@@ -898,43 +897,107 @@ __device__ __forceinline__ void process_segment_prefill(const StepArgs &a, int b
       store_table(a, tn, sh.lrows);
       __syncthreads();
     }
-    // all chunks of the piece, NBUF in flight, loads unconditional (indices
-    // past the end clamped to the last chunk)
-    const int last = nch - 1;
-    RowBuf2 buf[NBUF];
+    // Steps of two sub-chunks.  The stage loads of step s go to register set
+    // s % NR, issued NR steps ahead; in the steady state they are
+    // unconditional (steps past the end are clamped to the last), so the
+    // compiler counts them and waits only for the set it stores next.
+    const int nsteps = (nch + 1) >> 1;
+    auto step_key = [&](int s) { return (s < nsteps ? s : nsteps - 1) * STAGE_KEYS; };
+    auto compute = [&](int s) {
+      const Stage &sg = sh.stg[s & 1];
+      if constexpr (VERIFY) {
+        if (2 * s + cl < nch && nc > 0)
+          block_subchunk(sg, cl, kstart + (2 * s + cl) * CHUNK, lane, g, nc, qh, ql, st);
+      } else {
+        if (nc > 0) {
+          block_subchunk(sg, 0, kstart + 2 * s * CHUNK, lane, g, nc, qh, ql, st);
+          if (2 * s + 1 < nch)
+            block_subchunk(sg, 1, kstart + (2 * s + 1) * CHUNK, lane, g, nc, qh, ql, st);
+        }
+      }
+    };
+    StageIn in[NR];
 #pragma unroll
-    for (int k = 0; k < NBUF; ++k)
-      load_rows2(buf[k], a.k_cache, a.v_cache, sh.lrows + (k < last ? k : last) * CHUNK, n, j, g);
-    int i = 0;
-    for (; i + NBUF <= nch; i += NBUF) {
+    for (int k = 0; k < NR; ++k) stage_load(a, sh.lrows, step_key(k), in[k]);
+    stage_store(in[0], sh.stg[0]);
+    stage_load(a, sh.lrows, step_key(NR), in[0]);
+    __syncthreads();
+    int s = 0;
+    for (; s + NR < nsteps; s += NR) {
 #pragma unroll
-      for (int k = 0; k < NBUF; ++k) {
-        compute_chunk_prefill(buf[k], kstart + (i + k) * CHUNK, lane, qh, ql, vs);
-        const int inext = i + k + NBUF;
-        load_rows2(buf[k], a.k_cache, a.v_cache, sh.lrows + (inext < last ? inext : last) * CHUNK,
-                   n, j, g);
+      for (int k = 0; k < NR; ++k) {
+        compute(s + k);
+        stage_store(in[(k + 1) % NR], sh.stg[(s + k + 1) & 1]);
+        stage_load(a, sh.lrows, step_key(s + k + 1 + NR), in[(k + 1) % NR]);
+        __syncthreads();
       }
     }
 #pragma unroll
-    for (int k = 0; k < NBUF - 1; ++k)
-      if (i + k < nch) compute_chunk_prefill(buf[k], kstart + (i + k) * CHUNK, lane, qh, ql, vs);
+    for (int k = 0; k < NR; ++k) {
+      if (s + k < nsteps) {   // uniform
+        compute(s + k);
+        if (s + k + 1 < nsteps) stage_store(in[(k + 1) % NR], sh.stg[(s + k + 1) & 1]);
+        __syncthreads();
+      }
+    }
   }
 
-  // every wave writes the partials of its own columns
+  float lsum[2];
 #pragma unroll
-  for (int c = 0; c < 2; ++c) {
-    const float lsum = head_sum(vs.l[c]);
-    const int tk = tok(c);
-    if (tk < nt) {
+  for (int c = 0; c < 2; ++c) lsum[c] = st.o[4][c][0];
+  if constexpr (VERIFY) {
+    // Merge sub-chunk lane 1 into lane 0 (a one-chunk segment leaves lane 1
+    // empty).  The merge buffers share LDS with the stage buffers, which every
+    // wave has finished with at the last step's barrier.
+    if (nseg > 1) {   // uniform
+      if (cl == 1) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          if (c >= nc) break;
+          const int col = 16 * (2 * cq + c) + n;
+          float *row = sh.mrg[g][col];
+#pragma unroll
+          for (int dt = 0; dt < 4; ++dt) *reinterpret_cast<f32x4 *>(row + 16 * dt + 4 * j) = st.o[dt][c];
+          if (j == 0) {
+            sh.mrg_ml[g][col][0] = st.m[c];
+            sh.mrg_ml[g][col][1] = lsum[c];
+          }
+        }
+      }
+      __syncthreads();
+      if (cl == 0) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          if (c >= nc) break;
+          const int col = 16 * (2 * cq + c) + n;
+          const float *row = sh.mrg[g][col];
+          const float m1 = sh.mrg_ml[g][col][0], l1 = sh.mrg_ml[g][col][1];
+          const float M = fmaxf(st.m[c], m1);
+          const float c0 = st.m[c] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(st.m[c] - M);
+          const float c1 = m1 == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m1 - M);
+          lsum[c] = lsum[c] * c0 + l1 * c1;
+#pragma unroll
+          for (int dt = 0; dt < 4; ++dt)
+            st.o[dt][c] = st.o[dt][c] * c0 + *reinterpret_cast<const f32x4 *>(row + 16 * dt + 4 * j) * c1;
+          st.m[c] = M;
+        }
+      }
+    }
+  }
+  if (cl == 0) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int tk = tok(c);
+      if (c >= nc) break;
+      if (tk >= nt) continue;
       const size_t e = ((size_t)slot * a.tb + tk) * HQ + 8 * g + (n & 7);
       if (j == 0) {
-        a.part_ml[e * 2] = vs.m[c];
-        a.part_ml[e * 2 + 1] = lsum;
+        a.part_ml[e * 2] = st.m[c];
+        a.part_ml[e * 2 + 1] = lsum[c];
       }
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr)
-        *reinterpret_cast<f32x4 *>(a.part_o + e * D + 16 * j + 4 * rr) =
-            f32x4{vs.o[0][c][rr], vs.o[1][c][rr], vs.o[2][c][rr], vs.o[3][c][rr]};
+      for (int dt = 0; dt < 4; ++dt)
+        *reinterpret_cast<f32x4 *>(a.part_o + e * D + 16 * dt + 4 * j) = st.o[dt][c];
     }
   }
 }
@@ -1042,10 +1105,10 @@ __global__ __launch_bounds__(THREADS, 2) void attn_kernel(StepArgs a) {
     const KeyRange r = range_from(a, sh.req_len[u], sh.req_p0[u]);
     int b, blk;
     unit_of(a, u, b, blk);
-    if constexpr (MODE == 3)
-      process_segment_prefill<NBUF>(a, b, blk, r, x, y, w + u, sh);
+    if constexpr (MODE == 0)
+      process_segment<NBUF>(a, b, r, x, y, w + u, sh);
     else
-      process_segment<MODE, NBUF>(a, b, r, x, y, w + u, sh);
+      process_segment_block<MODE>(a, b, blk, r, x, y, w + u, sh);
   }
 }
 
@@ -1054,9 +1117,9 @@ void launch_attn(const StepArgs &a, hipStream_t stream) {
   if (a.L == 1)
     hipLaunchKernelGGL((attn_kernel<0, MUSEATTN_DECODE_NBUF>), grid, block, 0, stream, a);
   else if (a.L <= 8)
-    hipLaunchKernelGGL((attn_kernel<2, MUSEATTN_VERIFY_NBUF>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((attn_kernel<2, 1>), grid, block, 0, stream, a);
   else
-    hipLaunchKernelGGL((attn_kernel<3, MUSEATTN_PREFILL_NBUF>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((attn_kernel<3, 1>), grid, block, 0, stream, a);
 }
 
 }  // namespace museattn
