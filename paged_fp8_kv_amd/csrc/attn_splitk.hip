@@ -275,14 +275,18 @@ __device__ __forceinline__ StageMap stage_map(int t) {
   return m;
 }
 
-__device__ __forceinline__ void stage_load(const StepArgs &a, const uint32_t *lrows, int key0,
-                                           StageIn &in) {
+__device__ __forceinline__ void stage_load_row(const StepArgs &a, uint32_t row, StageIn &in) {
   const StageMap m = stage_map(threadIdx.x);
-  int kk = key0 + m.key;
-  kk = kk < MAX_SPLIT_LDS - 1 ? kk : MAX_SPLIT_LDS - 1;
-  const uint8_t *src = (m.v ? a.v_cache : a.k_cache) + (uint64_t)lrows[kk] * ROW + m.part * 32;
+  const uint8_t *src = (m.v ? a.v_cache : a.k_cache) + (uint64_t)row * ROW + m.part * 32;
   in.x[0] = *reinterpret_cast<const uint4 *>(src);
   in.x[1] = *reinterpret_cast<const uint4 *>(src + 16);
+}
+
+__device__ __forceinline__ void stage_load(const StepArgs &a, const uint32_t *lrows, int key0,
+                                           StageIn &in) {
+  int kk = key0 + stage_map(threadIdx.x).key;
+  kk = kk < MAX_SPLIT_LDS - 1 ? kk : MAX_SPLIT_LDS - 1;
+  stage_load_row(a, lrows[kk], in);
 }
 
 // Slot of chunk q of a V part: odd parts rotate by one.
@@ -553,18 +557,23 @@ struct TableIn {
   int32_t unit[MAX_SPLIT_LDS / THREADS];
 };
 
+// Only the first `nchunks` + 2 chunks' entries are loaded (the loops read at
+// most two chunks past a piece's end, for loads that are never used); the
+// rest get page 0, a valid row.
 __device__ __forceinline__ void load_table_in(const StepArgs &a, int b, const KeyRange &r,
-                                              int kstart, TableIn &in) {
+                                              int kstart, int nchunks, TableIn &in) {
   const int tid = threadIdx.x;
   const int shift = a.page_size == 1 ? 0 : 6;
   const int32_t *trow = a.table + (int64_t)b * a.table_stride;
+  const int need = (nchunks + 2) * CHUNK;
 #pragma unroll
   for (int it = 0; it < MAX_SPLIT_LDS / THREADS; ++it) {
     const int v = kstart + tid + it * THREADS;
     in.u[it] = v < r.klo ? r.klo : (v > r.khi ? r.khi : v);
   }
 #pragma unroll
-  for (int it = 0; it < MAX_SPLIT_LDS / THREADS; ++it) in.unit[it] = trow[in.u[it] >> shift];
+  for (int it = 0; it < MAX_SPLIT_LDS / THREADS; ++it)
+    in.unit[it] = it * THREADS < need ? trow[in.u[it] >> shift] : 0;
 }
 
 __device__ __forceinline__ void store_table(const StepArgs &a, const TableIn &in, uint32_t *lrows) {
@@ -620,7 +629,7 @@ __device__ __forceinline__ void process_segment(const StepArgs &a, int b, const 
 #pragma unroll
   for (int jt = 0; jt < 8; ++jt) pos[jt] = a.positions[b * a.L + (jt < a.L ? jt : a.L - 1)];
   TableIn tin;
-  load_table_in(a, b, r, r.kbase + x * CHUNK, tin);
+  load_table_in(a, b, r, r.kbase + x * CHUNK, PIECE_CHUNKS, tin);
   const QIn qin = load_q_in(a, b * a.L, n, j);   // head n of the token
   const f32x4 *w4 = reinterpret_cast<const f32x4 *>(a.wq + 16 * j);
   const f32x4 wv[4] = {w4[0], w4[1], w4[2], w4[3]};
@@ -669,7 +678,7 @@ __device__ __forceinline__ void process_segment(const StepArgs &a, int b, const 
     if (pc > 0) {
       __syncthreads();   // every wave is done with the previous rows
       TableIn tn;
-      load_table_in(a, b, r, kstart, tn);
+      load_table_in(a, b, r, kstart, PIECE_CHUNKS, tn);
       __builtin_amdgcn_sched_barrier(0);
       store_table(a, tn, sh.lrows);
       __syncthreads();
@@ -818,10 +827,22 @@ __device__ __forceinline__ void process_segment_block(const StepArgs &a, int b, 
   nc = nc < 0 ? 0 : (nc > 2 ? 2 : nc);
   auto tok = [&](int c) { return 4 * cq + 2 * c + (n >> 3); };   // unit token of the lane column
 
-  // One batch of loads: the first piece's table entries, the column tokens'
-  // positions and q, the q norm weights and (verify) the new rows' inputs.
+  // One batch of loads: the first piece's table entries (also, separately,
+  // those of the rows this thread stages in the first BLOCK_PREFETCH steps),
+  // the column tokens' positions and q, the q norm weights and (verify) the
+  // new rows' inputs.
+  const int shift = a.page_size == 1 ? 0 : 6;
+  const int nsteps0 = (piece_x(1) - x + 1) >> 1;
   TableIn tin;
-  load_table_in(a, b, r, r.kbase + x * CHUNK, tin);
+  load_table_in(a, b, r, r.kbase + x * CHUNK, piece_x(1) - x, tin);
+  int eu[NR], eunit[NR];
+#pragma unroll
+  for (int k = 0; k < NR; ++k) {
+    const int v = r.kbase + x * CHUNK + (k < nsteps0 ? k : nsteps0 - 1) * STAGE_KEYS +
+                  stage_map(tid).key;
+    eu[k] = v < r.klo ? r.klo : (v > r.khi ? r.khi : v);
+    eunit[k] = a.table[(int64_t)b * a.table_stride + (eu[k] >> shift)];
+  }
   int cpos[2];
   QIn2 qin[2];
 #pragma unroll
@@ -841,6 +862,33 @@ __device__ __forceinline__ void process_segment_block(const StepArgs &a, int b, 
     rin = load_row_in(a, b);
   }
   __builtin_amdgcn_sched_barrier(0);
+
+  // Verify: the block tokens whose new rows fall in this segment (only this
+  // work-group reads them; they are written below).
+  unsigned owned = 0;
+  if constexpr (VERIFY) {
+#pragma unroll
+    for (int jt = 0; jt < 8; ++jt) {
+      const int p = pos[jt];
+      const bool in = jt < a.L && p >= r.klo && p <= r.khi &&
+                      (p - r.kbase) / CHUNK >= x && (p - r.kbase) / CHUNK < y;
+      owned |= in ? 1u << jt : 0u;
+    }
+  }
+  // The first steps' stage loads leave now, from the thread's own table
+  // entries, so they overlap the set-up below -- unless the segment holds new
+  // rows, which must be written first.
+  const bool early = owned == 0;
+  StageIn in[NR];
+  if (early) {
+    const uint32_t units = (uint32_t)(a.num_rows >> shift);
+#pragma unroll
+    for (int k = 0; k < NR; ++k) {
+      uint32_t un = (uint32_t)eunit[k];
+      un = un < units ? un : units - 1;
+      stage_load_row(a, (un << shift) + (uint32_t)(eu[k] & (a.page_size - 1)), in[k]);
+    }
+  }
 
   __syncthreads();   // the previous segment is done with sh.cs, sh.lrows and the stage buffers
   if (a.sliding) {
@@ -869,17 +917,8 @@ __device__ __forceinline__ void process_segment_block(const StepArgs &a, int b, 
     for (int dt = 0; dt < 5; ++dt) st.o[dt][c] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   if constexpr (VERIFY) {
-    // New rows of the block tokens whose key falls in this segment: only this
-    // work-group reads them, so a workgroup release before the barrier orders
-    // the writes before its own loads.  (Prefill rows come from rows_kernel.)
-    unsigned owned = 0;
-#pragma unroll
-    for (int jt = 0; jt < 8; ++jt) {
-      const int p = pos[jt];
-      const bool in = jt < a.L && p >= r.klo && p <= r.khi &&
-                      (p - r.kbase) / CHUNK >= x && (p - r.kbase) / CHUNK < y;
-      owned |= in ? 1u << jt : 0u;
-    }
+    // the new rows: a workgroup release before the barrier orders the writes
+    // before this work-group's own loads.  (Prefill rows come from rows_kernel.)
     if (owned && wave < 4) write_new_rows(a, b, owned, pos, sh.cs, rin);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
   }
@@ -892,7 +931,7 @@ __device__ __forceinline__ void process_segment_block(const StepArgs &a, int b, 
     if (pc > 0) {
       __syncthreads();   // every wave is done with the previous rows
       TableIn tn;
-      load_table_in(a, b, r, kstart, tn);
+      load_table_in(a, b, r, kstart, py - px, tn);
       __builtin_amdgcn_sched_barrier(0);
       store_table(a, tn, sh.lrows);
       __syncthreads();
@@ -916,9 +955,10 @@ __device__ __forceinline__ void process_segment_block(const StepArgs &a, int b, 
         }
       }
     };
-    StageIn in[NR];
+    if (pc > 0 || !early) {   // uniform
 #pragma unroll
-    for (int k = 0; k < NR; ++k) stage_load(a, sh.lrows, step_key(k), in[k]);
+      for (int k = 0; k < NR; ++k) stage_load(a, sh.lrows, step_key(k), in[k]);
+    }
     stage_store(in[0], sh.stg[0]);
     stage_load(a, sh.lrows, step_key(NR), in[0]);
     __syncthreads();
