@@ -141,7 +141,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="2",
-                    help="workload id (0, 1, 2, 3s, 3f, 4; prefill blocks pf1f, pf1s, pf4f, "
+                    help="workload id (0, 1, 2, 3s, 3f, 4; batch shapes d16s, d16f, d32s, v16s, v16f, v32s, "
+                         "v32f; prefill blocks pf1f, pf1s, pf4f, "
                          "pf4s, pff0, pfs32, pff32, pff64)")
     ap.add_argument("--work-groups", type=int, default=0,
                     help="attention work-groups (0 = the library's choice)")

@@ -235,11 +235,27 @@ def config(cid: str, pool_rows: int | None = None) -> Workload:
     if cid in prefill:
         name, B, ctx, L, kind = prefill[cid]
         return make(name, 1100 + list(prefill).index(cid), B, L, ctx, kind, 1, 1.0, pool_rows)
+    # the decode page's batch shapes (its floor table): contexts spread over
+    # [60000, 100000], page size 1, pools just large enough (seed 1200 + index)
+    batch = {
+        "d16s": ("decode-b16-sliding-ctx60k-100k", 16, 1, SLIDING),
+        "d16f": ("decode-b16-full-ctx60k-100k", 16, 1, FULL),
+        "d32s": ("decode-b32-sliding-ctx60k-100k", 32, 1, SLIDING),
+        "v16s": ("verify-b16-L8-sliding-ctx60k-100k", 16, 8, SLIDING),
+        "v16f": ("verify-b16-L8-full-ctx60k-100k", 16, 8, FULL),
+        "v32s": ("verify-b32-L8-sliding-ctx60k-100k", 32, 8, SLIDING),
+        "v32f": ("verify-b32-L8-full-ctx60k-100k", 32, 8, FULL),
+    }
+    if cid in batch:
+        name, B, L, kind = batch[cid]
+        return make(name, 1200 + list(batch).index(cid), B, L, (60000, 100000), kind, 1, 1.0,
+                    pool_rows)
     raise KeyError(cid)
 
 
 CONFIG_IDS = ("0", "1", "2", "3s", "3f", "4")
 PREFILL_IDS = ("pf1f", "pf1s", "pf4f", "pf4s", "pff0", "pfs32", "pff32", "pff64")
+BATCH_IDS = ("d16s", "d16f", "d32s", "v16s", "v16f", "v32s", "v32f")
 
 
 # --------------------------------------------------------------------------
