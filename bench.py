@@ -36,6 +36,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
+OPROJ_HIDDEN = 8192   # the decoder layer's model width (the page's [T, 8192] activations)
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "attn_kernel_decode_b32_full_ctx60k-100k_pmc.txt")
 ATTN_SOURCE = os.path.join(ROOT, "paged_fp8_kv_amd", "csrc", "attn_splitk.hip")
 
@@ -159,6 +160,9 @@ def main():
     ap.add_argument("--graph-warmup", type=int, default=400,
                     help="untimed steps replayed from the captured graph before the timed "
                          "replay (back-to-back replays take ~10 ms to reach a steady state)")
+    ap.add_argument("--oproj", action="store_true",
+                    help="the step also runs the decoder layer's output projection "
+                         "(bf16 o [8192, 1024]); reported in the 'oproj' field")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="run a 1 GiB device copy first (PMC calibration runs)")
     args = ap.parse_args()
@@ -202,11 +206,20 @@ def main():
         del a, b
         log("calibration copy of 1 GiB done")
 
-    def step(events=None):
+    ow = yo = None
+    if args.oproj:
+        # the decoder layer's output projection after the step (bf16 [8192, 1024] weights)
+        ow = W.oproj_weight(w.seed, OPROJ_HIDDEN).to(dev)
+        yo = torch.empty(w.T, OPROJ_HIDDEN, dtype=torch.bfloat16, device=dev)
+
+    def step(events=None, oproj_events=None):
+        kw = {}
+        if args.oproj and events is None:   # attention events are taken on the plain step
+            kw = dict(o_weight=ow, y=yo, oproj_events=oproj_events)
         P.attn_step(d["qkv"], d["positions"], d["table"], d["seq_lens"], kp, vp, w.kv_scale,
                     w.page_size, w.layer_kind, out, q_norm_w=d["w_q"], k_norm_w=d["w_k"],
                     o_norm_w=d["w_o"], max_seq_len=w.max_seq_len, workspace=ws,
-                    work_groups=args.work_groups, attn_events=events)
+                    work_groups=args.work_groups, attn_events=events, **kw)
 
     for _ in range(args.warmup):
         step()
@@ -223,9 +236,14 @@ def main():
     def timed_eager():
         t0 = time.perf_counter()
         for i in range(args.steps):
-            step(evs[i])
+            step(None if args.oproj else evs[i])
         torch.cuda.synchronize()
         return time.perf_counter() - t0
+
+    def attn_evented():
+        for i in range(args.steps):
+            step(evs[i])
+        torch.cuda.synchronize()
 
     mode = "eager"
     if not args.eager:
@@ -254,12 +272,35 @@ def main():
     # the attention kernel's launch duration: HIP events recorded by the library
     # on the kernel's stream around each launch, over K eager steps (event
     # records captured inside a graph do not bracket the kernel on this runtime)
-    if mode == "graph":
-        timed_eager()
+    if mode == "graph" or args.oproj:
+        attn_evented()
     attn_ms = [hip_elapsed_ms(s0, e0) for s0, e0 in evs]
     attn_avg_ms = sum(attn_ms) / len(attn_ms)
     log(f"timed {args.steps} steps ({mode}): {ms_per_step * 1e3:.1f} us/step; attention kernel "
         f"avg {attn_avg_ms * 1e3:.1f} us (min {min(attn_ms) * 1e3:.1f})")
+
+    oproj = None
+    if args.oproj:
+        oevs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                for _ in range(args.steps)]
+        for pair in oevs:
+            for e in pair:
+                e.record()
+        torch.cuda.synchronize()
+        for i in range(args.steps):
+            step(oproj_events=oevs[i])
+        torch.cuda.synchronize()
+        o_ms = [hip_elapsed_ms(s0, e0) for s0, e0 in oevs]
+        o_avg = sum(o_ms) / len(o_ms)
+        obytes = OPROJ_HIDDEN * 1024 * 2 + w.T * 1024 * 2 + w.T * OPROJ_HIDDEN * 2
+        oproj = {"kernel": "oproj_kernel (y = out . o^T, bf16 MFMA, fp32 sums)",
+                 "hidden": OPROJ_HIDDEN, "bound": "hbm", "algorithmic_bytes_per_launch": obytes,
+                 "avg_launch_us": round(o_avg * 1e3, 2),
+                 "achieved": round(obytes / (o_avg * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBS,
+                 "unit": "GB/s", "frac": round(obytes / (o_avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                 "avg_launch_us_from": f"HIP events around each of {args.steps} eager launches"}
+        log(f"o-projection kernel avg {o_avg * 1e3:.2f} us ({oproj['achieved']} GB/s on "
+            f"{obytes / 1e6:.1f} MB)")
 
     cold = None
     if args.cold_reps > 0:
@@ -360,8 +401,10 @@ def main():
                    "kv_bytes": kv, "attn_flops": w.attn_flops, "pool_rows": w.num_rows,
                    "seed": w.seed,
                    "work_groups": P.work_groups(w.B, w.L, w.max_seq_len, w.layer_kind,
-                                                args.work_groups)},
+                                                args.work_groups),
+                   "step_includes_oproj": bool(args.oproj)},
         "cold_cache_graph_replay": cold,
+        "oproj": oproj,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

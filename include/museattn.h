@@ -71,6 +71,7 @@ enum museattn_layer_kind { MUSEATTN_FULL = 0, MUSEATTN_SLIDING = 1 };
 #define MUSEATTN_QKV_WIDTH 2304
 #define MUSEATTN_OUT_WIDTH 1024
 #define MUSEATTN_ROW_BYTES 128
+#define MUSEATTN_MAX_HIDDEN 65536   /* o-projection output features */
 
 enum museattn_status {
   MUSEATTN_OK = 0,
@@ -163,6 +164,34 @@ int museattn_attn_step_profiled(const void *qkv, const int32_t *positions, const
                                 int64_t num_rows, const museattn_params *params, void *workspace,
                                 size_t workspace_bytes, void *attn_start_event,
                                 void *attn_end_event);
+
+/* The attention output projection of the decoder layer (task page "Whole
+ * decoder layer", section "What to compute": the gated attention output times
+ * o^T; on one GPU the all-reduce that follows is the identity):
+ *   y[t][n] = sum_k a[t][k] * o_weight[n][k],   k < 1024 (16 heads x 64 dims),
+ * bf16 operands, fp32 accumulation, bf16 y (round to nearest even).
+ *   a         bf16 [T][1024], 16-byte aligned (the step's `out`)
+ *   o_weight  bf16 [hidden][1024], row n = output feature n, 16-byte aligned
+ *   T         >= 1 tokens
+ *   hidden    output features, a multiple of 64 in [64, MUSEATTN_MAX_HIDDEN]
+ *   y         bf16 [T][hidden], 8-byte aligned, overlapping neither a nor o_weight
+ *   stream    hipStream_t the work is enqueued on
+ * Device pointers, owned by the caller; nothing is allocated.  Statuses:
+ * MUSEATTN_ERR_NULL, _PARAM (T or hidden), _ALIGN, _ALIAS, _LAUNCH. */
+int museattn_oproj(const void *a, const void *o_weight, int T, int hidden, void *y, void *stream);
+
+/* museattn_attn_step followed by museattn_oproj on its output, on the same
+ * stream (the step's `out` still receives the gated output; the projection
+ * reads it back from the cache hierarchy).  The two optional caller-created
+ * hipEvent_t are recorded around the projection kernel.  Checks both calls'
+ * arguments before enqueuing anything (y must also not overlap qkv). */
+int museattn_attn_step_oproj(const void *qkv, const int32_t *positions, const int32_t *table,
+                             const int32_t *seq_lens, void *k_cache, void *v_cache, float kv_scale,
+                             int page_size, int layer_kind, void *out, void *stream, int B, int L,
+                             int table_stride, int max_seq_len, int64_t num_rows,
+                             const museattn_params *params, void *workspace,
+                             size_t workspace_bytes, const void *o_weight, int hidden, void *y,
+                             void *oproj_start_event, void *oproj_end_event);
 
 /* Attention work-groups the library launches for these shapes
  * (params->work_groups = 0 chooses). */

@@ -18,6 +18,10 @@ program (numpy matmul and exp are the only library steps):
                                                2048 positions p-2047..p (sliding)
     out = rmsnorm(a) * sigmoid(gate)           per head, bf16 [B, L, 16*64]
 
+and the output projection that follows it in the decoder layer (task page
+"Whole decoder layer", section "What to compute"; the all-reduce after it is
+the identity on one GPU):  y = out @ o^T, o [hidden, 1024].
+
 Readings where the page is silent:
   * qkv row layout [q 16x64 | k 2x64 | v 2x64 | gate 16x64], head-major.
   * query head h reads KV head h // 8 (contiguous GQA groups of 8).
@@ -253,3 +257,11 @@ def attn_step(qkv, positions, table, k_pool, v_pool, *, B, L, page_size, layer_k
                window if sliding else None, tokens)
     out = gated_output(a, gate, w_o, eps)
     return out.reshape(B, L, HQ * D), kbyte, vbyte
+
+
+def oproj(a, o_weight):
+    """The attention output projection: y[t, n] = sum_k a[t, k] * o[n, k]
+    (a [T, 1024], o [hidden, 1024]); float64."""
+    a = np.asarray(a, dtype=np.float64)
+    o_weight = np.asarray(o_weight, dtype=np.float64)
+    return a @ o_weight.T

@@ -32,7 +32,7 @@ STATUS = {
 # every symbol include/museattn.h declares
 EXPORTS = ("museattn_abi_version", "museattn_strerror", "museattn_workspace_bytes",
            "museattn_check_args", "museattn_attn_step", "museattn_attn_step_profiled",
-           "museattn_work_groups")
+           "museattn_work_groups", "museattn_oproj", "museattn_attn_step_oproj")
 
 
 class Params(ctypes.Structure):
@@ -82,6 +82,10 @@ def lib() -> ctypes.CDLL:
                                                   ctypes.c_size_t]
         L.museattn_attn_step_profiled.restype = i32
         L.museattn_attn_step_profiled.argtypes = L.museattn_attn_step.argtypes + [vp, vp]
+        L.museattn_attn_step_oproj.restype = i32
+        L.museattn_attn_step_oproj.argtypes = L.museattn_attn_step.argtypes + [vp, i32, vp, vp, vp]
+        L.museattn_oproj.restype = i32
+        L.museattn_oproj.argtypes = [vp, vp, i32, i32, vp, vp]
         _lib = L
     return _lib
 
@@ -136,7 +140,8 @@ def _need(cond, msg):
 def attn_step(qkv, positions, table, seq_lens, k_cache, v_cache, kv_scale, page_size,
               layer_kind, out, stream=None, *, q_norm_w, k_norm_w, o_norm_w, max_seq_len,
               workspace=None, eps=DEFAULT_EPS, q_scale=DEFAULT_Q_SCALE,
-              rope_base=DEFAULT_ROPE_BASE, work_groups=0, attn_events=None):
+              rope_base=DEFAULT_ROPE_BASE, work_groups=0, attn_events=None, o_weight=None,
+              y=None, oproj_events=None):
     """One attention step on torch tensors (see include/museattn.h).
 
     qkv bf16 [B*L, 2304]; positions int32 [B*L]; table int32 [B, stride];
@@ -146,7 +151,9 @@ def attn_step(qkv, positions, table, seq_lens, k_cache, v_cache, kv_scale, page_
     (then allocated here with torch).  stream: a torch.cuda.Stream, a raw
     hipStream_t int, or None for the current stream.  attn_events: optional
     (start, end) torch.cuda.Event pair recorded around the attention kernel
-    (museattn_attn_step_profiled)."""
+    (museattn_attn_step_profiled).  o_weight (bf16 [hidden, 1024]) and y
+    (bf16 [B*L, hidden]) given: the output projection follows the step
+    (museattn_attn_step_oproj), oproj_events around its kernel."""
     import torch
 
     B = int(seq_lens.shape[0])
@@ -189,6 +196,17 @@ def attn_step(qkv, positions, table, seq_lens, k_cache, v_cache, kv_scale, page_
             int(layer_kind), out.data_ptr(), stream_ptr, B, L, int(table.shape[1]),
             int(max_seq_len), int(num_rows), ctypes.byref(params), workspace.data_ptr(),
             int(workspace.numel()))
+    if o_weight is not None or y is not None:
+        _need(o_weight is not None and y is not None, "o_weight and y go together")
+        _need(attn_events is None, "attn_events are not recorded with the projection")
+        hidden = _check_oproj(out.view(T, OUT_WIDTH), o_weight, y, dev)
+        ev = oproj_events or (None, None)
+        st = lib().museattn_attn_step_oproj(*args, o_weight.data_ptr(), hidden, y.data_ptr(),
+                                            ev[0].cuda_event if ev[0] is not None else None,
+                                            ev[1].cuda_event if ev[1] is not None else None)
+        if st != OK:
+            raise MuseAttnError(st, "museattn_attn_step_oproj")
+        return out
     if attn_events is None:
         st = lib().museattn_attn_step(*args)
     else:
@@ -197,3 +215,34 @@ def attn_step(qkv, positions, table, seq_lens, k_cache, v_cache, kv_scale, page_
     if st != OK:
         raise MuseAttnError(st, "museattn_attn_step")
     return out
+
+
+def _check_oproj(a, o_weight, y, dev) -> int:
+    import torch
+    for name, t in (("a", a), ("o_weight", o_weight), ("y", y)):
+        _need(t.is_cuda and t.device == dev, f"{name} must be on {dev}")
+        _need(t.is_contiguous() and t.dtype == torch.bfloat16, f"{name} must be contiguous bf16")
+    _need(o_weight.dim() == 2 and o_weight.shape[1] == OUT_WIDTH, "o_weight must be [hidden, 1024]")
+    hidden = int(o_weight.shape[0])
+    _need(a.dim() == 2 and a.shape[1] == OUT_WIDTH, "a must be [T, 1024]")
+    _need(tuple(y.shape) == (a.shape[0], hidden), "y must be [T, hidden]")
+    return hidden
+
+
+def oproj(a, o_weight, y, stream=None):
+    """museattn_oproj: y = a @ o_weight^T (bf16 in, fp32 sums, bf16 out) on
+    torch tensors; a [T, 1024], o_weight [hidden, 1024], y [T, hidden]."""
+    import torch
+
+    hidden = _check_oproj(a, o_weight, y, a.device)
+    if stream is None:
+        stream_ptr = torch.cuda.current_stream(a.device).cuda_stream
+    elif hasattr(stream, "cuda_stream"):
+        stream_ptr = stream.cuda_stream
+    else:
+        stream_ptr = int(stream)
+    st = lib().museattn_oproj(a.data_ptr(), o_weight.data_ptr(), int(a.shape[0]), hidden,
+                              y.data_ptr(), stream_ptr)
+    if st != OK:
+        raise MuseAttnError(st, "museattn_oproj")
+    return y

@@ -7,4 +7,6 @@ namespace museattn {
 void launch_attn(const StepArgs &a, hipStream_t stream);
 void launch_combine(const StepArgs &a, hipStream_t stream);
 void launch_rows(const StepArgs &a, hipStream_t stream);
+void launch_oproj(const uint16_t *a, const uint16_t *o, uint16_t *y, int T, int N,
+                  hipStream_t stream);
 }  // namespace museattn

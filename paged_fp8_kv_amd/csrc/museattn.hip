@@ -205,4 +205,57 @@ int museattn_attn_step(const void *qkv, const int32_t *positions, const int32_t 
                                      nullptr, nullptr);
 }
 
+namespace {
+// The projection's own arguments (the gated output a is bf16 [T][1024]).
+int check_oproj(const void *a, const void *o_weight, int T, int hidden, const void *y) {
+  if (!a || !o_weight || !y) return MUSEATTN_ERR_NULL;
+  if (T < 1 || hidden < 64 || hidden > MUSEATTN_MAX_HIDDEN || hidden % 64) return MUSEATTN_ERR_PARAM;
+  if (!museattn::aligned(a, 16) || !museattn::aligned(o_weight, 16) || !museattn::aligned(y, 8))
+    return MUSEATTN_ERR_ALIGN;
+  const uintptr_t y0 = (uintptr_t)y, y1 = y0 + (uintptr_t)T * hidden * 2;
+  const uintptr_t a0 = (uintptr_t)a, a1 = a0 + (uintptr_t)T * MUSEATTN_OUT_WIDTH * 2;
+  const uintptr_t w0 = (uintptr_t)o_weight, w1 = w0 + (uintptr_t)hidden * MUSEATTN_OUT_WIDTH * 2;
+  if ((y0 < a1 && a0 < y1) || (y0 < w1 && w0 < y1)) return MUSEATTN_ERR_ALIAS;
+  return MUSEATTN_OK;
+}
+}  // namespace
+
+int museattn_oproj(const void *a, const void *o_weight, int T, int hidden, void *y, void *stream) {
+  const int st = check_oproj(a, o_weight, T, hidden, y);
+  if (st != MUSEATTN_OK) return st;
+  (void)hipGetLastError();
+  museattn::launch_oproj(static_cast<const uint16_t *>(a), static_cast<const uint16_t *>(o_weight),
+                         static_cast<uint16_t *>(y), T, hidden, static_cast<hipStream_t>(stream));
+  return hipGetLastError() == hipSuccess ? MUSEATTN_OK : MUSEATTN_ERR_LAUNCH;
+}
+
+int museattn_attn_step_oproj(const void *qkv, const int32_t *positions, const int32_t *table,
+                             const int32_t *seq_lens, void *k_cache, void *v_cache, float kv_scale,
+                             int page_size, int layer_kind, void *out, void *stream, int B, int L,
+                             int table_stride, int max_seq_len, int64_t num_rows,
+                             const museattn_params *params, void *workspace,
+                             size_t workspace_bytes, const void *o_weight, int hidden, void *y,
+                             void *oproj_start_event, void *oproj_end_event) {
+  int st = museattn_check_args(qkv, positions, table, seq_lens, k_cache, v_cache, kv_scale,
+                               page_size, layer_kind, out, B, L, table_stride, max_seq_len,
+                               num_rows, params, workspace, workspace_bytes);
+  if (st != MUSEATTN_OK) return st;
+  const int T = B * L;
+  st = check_oproj(out, o_weight, T, hidden, y);
+  if (st != MUSEATTN_OK) return st;
+  const uintptr_t y0 = (uintptr_t)y, y1 = y0 + (uintptr_t)T * hidden * 2;
+  const uintptr_t q0 = (uintptr_t)qkv, q1 = q0 + (uintptr_t)T * MUSEATTN_QKV_WIDTH * 2;
+  if (y0 < q1 && q0 < y1) return MUSEATTN_ERR_ALIAS;
+  st = museattn_attn_step(qkv, positions, table, seq_lens, k_cache, v_cache, kv_scale, page_size,
+                          layer_kind, out, stream, B, L, table_stride, max_seq_len, num_rows,
+                          params, workspace, workspace_bytes);
+  if (st != MUSEATTN_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (oproj_start_event) (void)hipEventRecord(static_cast<hipEvent_t>(oproj_start_event), s);
+  museattn::launch_oproj(static_cast<const uint16_t *>(out), static_cast<const uint16_t *>(o_weight),
+                         static_cast<uint16_t *>(y), T, hidden, s);
+  if (oproj_end_event) (void)hipEventRecord(static_cast<hipEvent_t>(oproj_end_event), s);
+  return hipGetLastError() == hipSuccess ? MUSEATTN_OK : MUSEATTN_ERR_LAUNCH;
+}
+
 }  // extern "C"

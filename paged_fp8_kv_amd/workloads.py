@@ -350,3 +350,23 @@ class LogicalPool:
         if not hit[0]:
             raise KeyError(f"row {row} is not part of this logical pool")
         self.data[i[0]] = value
+
+
+# --------------------------------------------------------------------------
+# Output-projection inputs (plumbing): o [hidden, 1024] with N(0, 1/64^2)
+# entries rounded to bf16 (the spread of a trained projection's weights), and
+# standalone projection inputs a ~ N(0, 1/4) rounded to bf16.
+# --------------------------------------------------------------------------
+
+def oproj_weight(seed: int, hidden: int = 8192):
+    import torch
+    rng = np.random.default_rng([seed, 9, hidden])
+    return torch.from_numpy(rng.standard_normal((hidden, 1024)).astype(np.float32) / 64.0
+                            ).to(torch.bfloat16)
+
+
+def oproj_input(seed: int, T: int):
+    import torch
+    rng = np.random.default_rng([seed, 10, T])
+    return torch.from_numpy(rng.standard_normal((T, 1024)).astype(np.float32) * 0.5
+                            ).to(torch.bfloat16)

@@ -134,3 +134,18 @@ def test_attn_step_refuses_cpu_tensors():
                     torch.zeros(1, 1, 1024, dtype=torch.bfloat16),
                     q_norm_w=torch.ones(64), k_norm_w=torch.ones(64), o_norm_w=torch.ones(64),
                     max_seq_len=1)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(a=0), -1), (dict(o=0), -1), (dict(y=0), -1),
+    (dict(T=0), -8), (dict(hidden=24), -8), (dict(hidden=0), -8), (dict(hidden=65552), -8),
+    (dict(a=A["qkv"] + 8), -6), (dict(o=A["wq"] + 4), -6), (dict(y=A["out"] + 4), -6),
+    (dict(y=A["qkv"]), -9),
+])
+def test_oproj_invalid_arguments_are_rejected(kw, status):
+    """Host-side checks of museattn_oproj: they return before any device call."""
+    lib = P.lib()
+    args = dict(a=A["qkv"], o=A["wq"], T=4, hidden=8192, y=A["out"])
+    args.update(kw)
+    st = lib.museattn_oproj(args["a"], args["o"], args["T"], args["hidden"], args["y"], None)
+    assert st == status

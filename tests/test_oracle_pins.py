@@ -366,3 +366,43 @@ def test_requests_are_independent():
     w.qkv = qkv
     o2, _, _ = _run_oracle(w, kp.copy(), vp.copy())
     assert np.array_equal(o1[1:], o2[1:]) and not np.array_equal(o1[0], o2[0])
+
+
+# --------------------------------------------------------------------------
+# The output projection (task page "Whole decoder layer", section "What to
+# compute": y = out @ o^T): pinned by closed forms and brute force, not by the
+# matmul it calls.
+# --------------------------------------------------------------------------
+
+def test_oproj_permutation_rows_select_inputs():
+    rng = np.random.default_rng(7)
+    a = rng.standard_normal((5, 1024))
+    perm = rng.permutation(1024)[:48]
+    o = np.zeros((48, 1024))
+    o[np.arange(48), perm] = 1.0          # row n picks input feature perm[n]
+    y = O.oproj(a, o)
+    assert np.array_equal(y, a[:, perm])
+    o2 = o * 3.0                           # linear in o
+    assert np.array_equal(O.oproj(a, o2), 3.0 * a[:, perm])
+
+
+def test_oproj_brute_force_on_small_inputs():
+    rng = np.random.default_rng(8)
+    a = rng.standard_normal((3, 1024))
+    o = rng.standard_normal((16, 1024))
+    y = O.oproj(a, o)
+    for t in range(3):
+        for n in range(16):
+            want = math.fsum(float(a[t, k]) * float(o[n, k]) for k in range(1024))
+            assert abs(y[t, n] - want) <= 1e-9 * (1 + abs(want))
+
+
+def test_oproj_catches_a_transposed_operand(monkeypatch):
+    # a square, non-symmetric o: using o instead of o^T must be seen
+    rng = np.random.default_rng(9)
+    a = rng.standard_normal((4, 1024))
+    o = rng.standard_normal((1024, 1024))
+    brute = np.array([[math.fsum(a[t] * o[n]) for n in range(0, 1024, 97)] for t in range(4)])
+    assert np.allclose(O.oproj(a, o)[:, ::97], brute, rtol=1e-9, atol=1e-9)
+    monkeypatch.setattr(O, "oproj", lambda a_, o_: np.asarray(a_) @ np.asarray(o_))
+    assert not np.allclose(O.oproj(a, o)[:, ::97], brute, rtol=1e-3, atol=1e-3)
