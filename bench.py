@@ -35,7 +35,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-MFMA_BF16_PEAK_TFLOPS = 2500.0
+MFMA_F16_PEAK_TFLOPS = 2500.0
 OPROJ_HIDDEN = 8192   # the decoder layer's model width (the page's [T, 8192] activations)
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "attn_kernel_decode_b32_full_ctx60k-100k_pmc.txt")
 ATTN_SOURCE = os.path.join(ROOT, "paged_fp8_kv_amd", "csrc", "attn_splitk.hip")
@@ -367,12 +367,12 @@ def main():
                     "algorithmic_bytes_per_launch": kv,
                     "avg_launch_us": round(attn_avg_ms * 1e3, 2), "avg_launch_us_from": timing_note}
     else:
-        # a prefill block: 4 * 64 FLOPs per (visible key, token, query head), a
-        # bf16 MFMA contraction; each key's bytes are reused by up to L tokens
+        # a prefill block: 4 * 64 FLOPs per (visible key, token, query head), an
+        # fp16 MFMA contraction; each key's bytes are reused by up to L tokens
         fl = w.attn_flops
         value = fl / (ms_per_step * 1e-3) / 1e12
-        unit, peak = "TFLOP/s", MFMA_BF16_PEAK_TFLOPS
-        metric = "us/step and attention TFLOP/s (% of bf16 MFMA peak), prefill block, 1 GPU"
+        unit, peak = "TFLOP/s", MFMA_F16_PEAK_TFLOPS
+        metric = "us/step and attention TFLOP/s (% of fp16 MFMA peak), prefill block, 1 GPU"
         achieved = fl / (attn_avg_ms * 1e-3) / 1e12
         roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                     "unit": unit, "frac": round(achieved / peak, 4), "traffic": None,

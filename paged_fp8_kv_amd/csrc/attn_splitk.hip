@@ -69,6 +69,19 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t x, uint32_t y) {
   return r;
 }
 
+// Blocks: the same 8 codes in fp16 (also exact: every E4M3 value is an fp16
+// value).
+__device__ __forceinline__ f16x8 fp8x8_to_f16(uint32_t x, uint32_t y) {
+  const f16x2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x, 1.0f, false);
+  const f16x2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x, 1.0f, true);
+  const f16x2 c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(y, 1.0f, false);
+  const f16x2 d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(y, 1.0f, true);
+  f16x8 r;
+  r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
+  r[4] = c[0]; r[5] = c[1]; r[6] = d[0]; r[7] = d[1];
+  return r;
+}
+
 // 4x4 byte transpose: y_k byte i = x_i byte k.
 __device__ __forceinline__ void transpose4x4(uint32_t x0, uint32_t x1, uint32_t x2, uint32_t x3,
                                              uint32_t &y0, uint32_t &y1, uint32_t &y2,
@@ -205,16 +218,16 @@ __device__ __forceinline__ void compute_chunk(const RowBuf &rb, int u0, int lane
 // 32-key sub-chunks) that its 8 waves share:
 //  * staging: thread t loads 32 B of key t/8's K row (t%8 < 4) or V row
 //    (t%8 >= 4), so 4 lanes read one whole 128-B row; the bytes are converted
-//    to bf16 once for the work-group and written, key-major, into one of two
+//    to fp16 (exactly) once for the work-group and written, key-major, into one of two
 //    LDS stage buffers (rows padded against bank conflicts).  The loads run
 //    BLOCK_PREFETCH steps ahead in registers; one barrier per step.
 //  * S^T (32 keys x 16 columns) per sub-chunk and column tile: 2 key tiles x
-//    2 K-steps of v_mfma_f32_16x16x32_bf16; A = K rows from LDS (K-step kk:
-//    dims 32kk + 8j..+7 in lane (n, j)), B = Q^T from registers as bf16 hi +
-//    lo, so the product keeps ~16 significant bits of q.
+//    2 K-steps of v_mfma_f32_16x16x32_f16; A = K rows from LDS (K-step kk:
+//    dims 32kk + 8j..+7 in lane (n, j)), B = Q^T from registers in fp16 (11
+//    significant bits of q, scaled by a power of two if it would overflow).
 //  * S^T leaves column n's scores for keys 4j..4j+3 (key tile 0) and
 //    16+4j..16+4j+3 (key tile 1) in lane (n, j): the B operand layout of
-//    O^T = V^T . P^T, so P stays in place, rounded to bf16.
+//    O^T = V^T . P^T, so P stays in place, rounded to fp16.
 //  * V^T tiles come from the row-major stage through the gfx950 transposing
 //    LDS read (ds_read_b64_tr_b16): within a 16-lane group, lane s names 4
 //    dims of key k0 + s/4 and lane i receives dim i of those 4 keys.
@@ -225,7 +238,7 @@ __device__ __forceinline__ void compute_chunk(const RowBuf &rb, int u0, int lane
 // column tiles per KV head): wave w takes KV head w % 2, column tiles 2(w/2)
 // and 2(w/2) + 1, and both sub-chunks of each step.
 constexpr int STAGE_KEYS = 64;
-constexpr int KROW = 272;   // LDS bytes per key of the K stage: 2 heads x 64 bf16, + 16
+constexpr int KROW = 272;   // LDS bytes per key of the K stage: 2 heads x 64 fp16, + 16
 constexpr int VROW = 288;   // of the V stage: + 32 (a transposing read spans 4 rows x 32 B)
 
 struct Stage {
@@ -240,6 +253,9 @@ struct BlockState {
   f32x4 negm[2];   // -m (0 while m = -inf), the accumulator the scores start from
   float m[2];      // the column's reference max (log2 units)
   int lo[2], hi[2];   // visible key range of the lane column's token, inclusive
+  int e[2];           // q of the lane column is held as q * 2^-e in fp16 (e = 0
+                      // unless |q| * qmul reaches 2^15)
+  bool scaled;        // some column of the wave has e > 0 (wave-uniform)
 };
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -253,7 +269,7 @@ struct StageIn {
 // Which 32 bytes thread t stages: wave w takes keys 8w..8w+7 of the step.
 // Lanes 0-31 take K rows (key 8w + l%8, part [0, 2, 1, 3][l/8]); lanes 32-63
 // take V rows, each group of 8 lanes 4 keys x 2 adjacent parts.  A part is 32
-// fp8 bytes = 64 bf16 bytes = 4 chunks of 16 B, written one chunk per
+// fp8 bytes = 64 fp16 bytes = 4 chunks of 16 B, written one chunk per
 // ds_write_b128.  In the V stage an odd part's chunk q sits at slot (q - 1) %
 // 4; with this order the 8 (or 16) lanes an LDS pass serves hit distinct
 // banks, for stores as well as for the operand reads.
@@ -295,24 +311,24 @@ __device__ __forceinline__ int v_slot(int part, int q) { return (q - (part & 1))
 __device__ __forceinline__ void stage_store(const StageIn &in, Stage &st) {
   const StageMap m = stage_map(threadIdx.x);
   uint8_t *dst = m.v ? st.v + m.key * VROW + m.part * 64 : st.k + m.key * KROW + m.part * 64;
-  const bf16x8 c[4] = {fp8x8_to_bf16(in.x[0].x, in.x[0].y), fp8x8_to_bf16(in.x[0].z, in.x[0].w),
-                       fp8x8_to_bf16(in.x[1].x, in.x[1].y), fp8x8_to_bf16(in.x[1].z, in.x[1].w)};
+  const f16x8 c[4] = {fp8x8_to_f16(in.x[0].x, in.x[0].y), fp8x8_to_f16(in.x[0].z, in.x[0].w),
+                      fp8x8_to_f16(in.x[1].x, in.x[1].y), fp8x8_to_f16(in.x[1].z, in.x[1].w)};
 #pragma unroll
   for (int q = 0; q < 4; ++q)
-    *reinterpret_cast<bf16x8 *>(dst + 16 * (m.v ? v_slot(m.part, q) : q)) = c[q];
+    *reinterpret_cast<f16x8 *>(dst + 16 * (m.v ? v_slot(m.part, q) : q)) = c[q];
 }
 
 // A operand of S^T: key tile t of sub-chunk sc, K-step kk, KV head g.
-__device__ __forceinline__ bf16x8 k_operand(const Stage &st, int sc, int t, int kk, int n, int j,
-                                            int g) {
-  return *reinterpret_cast<const bf16x8 *>(st.k + (32 * sc + 16 * t + n) * KROW + g * 128 +
+__device__ __forceinline__ f16x8 k_operand(const Stage &st, int sc, int t, int kk, int n, int j,
+                                           int g) {
+  return *reinterpret_cast<const f16x8 *>(st.k + (32 * sc + 16 * t + n) * KROW + g * 128 +
                                            kk * 64 + j * 16);
 }
 
 // A operand of O^T = V^T . P^T: dim tile dt of sub-chunk sc, KV head g.  Lane
 // (n, j) receives dim 16dt + n of keys 4j..4j+3 (elements 0-3) and
 // 16+4j..16+4j+3 (elements 4-7), the keys whose P it holds.
-__device__ __forceinline__ bf16x8 v_operand(const Stage &st, int sc, int dt, int n, int j, int g) {
+__device__ __forceinline__ f16x8 v_operand(const Stage &st, int sc, int dt, int n, int j, int g) {
   // dims 16dt + 4(n%4).. of head g: part 2g + dt/2, chunk 2(dt%2) + (n%4)/2, 8 B in
   const int part = 2 * g + (dt >> 1), q = 2 * (dt & 1) + ((n & 3) >> 1);
   const uint8_t *p = st.v + (32 * sc + 4 * j + (n >> 2)) * VROW + part * 64 + 16 * v_slot(part, q) +
@@ -321,7 +337,7 @@ __device__ __forceinline__ bf16x8 v_operand(const Stage &st, int sc, int dt, int
   const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p + 16 * VROW));
   typedef short i16x8 __attribute__((ext_vector_type(8)));
   const i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-  return __builtin_bit_cast(bf16x8, v);
+  return __builtin_bit_cast(f16x8, v);
 }
 
 // IEEE maximum (gfx950 v_maximum3_f32; no operand canonicalisation needed).
@@ -331,9 +347,13 @@ __device__ __forceinline__ float fmax_ieee(float a, float b) { return __builtin_
 // sub-chunk whose first key is u0.  s0, s1: the two key tiles of S^T, already
 // relative to the reference max (the products start from -m), or raw while
 // the column has no reference yet.
-__device__ __forceinline__ void block_tile(f32x4 s0, f32x4 s1, const bf16x8 (&va)[4], bf16x8 ones,
+__device__ __forceinline__ void block_tile(f32x4 s0, f32x4 s1, const f16x8 (&va)[4], f16x8 ones,
                                            int u0, int j, BlockState &st, int c) {
   float sc[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+  if (st.scaled) {   // uniform; products of q * 2^-e back to log2 units
+#pragma unroll
+    for (int i = 0; i < 8; ++i) sc[i] = ldexpf(sc[i], st.e[c]);
+  }
   const int lo = st.lo[c], hi = st.hi[c];
   if (u0 < lo || u0 + CHUNK - 1 > hi) {
     // score i is key u0 + 4j + off_i, off_i = 16 (i / 4) + i % 4
@@ -365,49 +385,46 @@ __device__ __forceinline__ void block_tile(f32x4 s0, f32x4 s1, const bf16x8 (&va
     for (int i = 0; i < 8; ++i) sc[i] -= d;
 #pragma unroll
     for (int dt = 0; dt < 5; ++dt) st.o[dt][c] *= alpha;
-    const float nm = st.m[c] == -INFINITY ? 0.0f : -st.m[c];
+    const float nm = st.m[c] == -INFINITY ? 0.0f : ldexpf(-st.m[c], -st.e[c]);
     st.negm[c] = f32x4{nm, nm, nm, nm};
   }
   float pv[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) pv[i] = __builtin_amdgcn_exp2f(sc[i]);
-  bf16x8 ph;
+  f16x8 ph;
 #pragma unroll
   for (int i = 0; i < 8; i += 2) {
-    const bf16x2 h = __builtin_convertvector((f32x2{pv[i], pv[i + 1]}), bf16x2);
+    const f16x2 h = __builtin_convertvector((f32x2{pv[i], pv[i + 1]}), f16x2);
     ph[i] = h[0];
     ph[i + 1] = h[1];
   }
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
-    st.o[dt][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[dt], ph, st.o[dt][c], 0, 0, 0);
-  st.o[4][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, ph, st.o[4][c], 0, 0, 0);
+    st.o[dt][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va[dt], ph, st.o[dt][c], 0, 0, 0);
+  st.o[4][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, ph, st.o[4][c], 0, 0, 0);
 }
 
 // One sub-chunk (32 keys from u0) for the wave's nc live column tiles.
 __device__ __forceinline__ void block_subchunk(const Stage &stg, int sc, int u0, int lane, int g,
-                                               int nc, const bf16x8 (&qh)[2][2],
-                                               const bf16x8 (&ql)[2][2], BlockState &st) {
+                                               int nc, const f16x8 (&qf)[2][2], BlockState &st) {
   const int n = lane & 15, j = lane >> 4;
-  bf16x8 ka[2][2], va[4];
+  f16x8 ka[2][2], va[4];
 #pragma unroll
   for (int t = 0; t < 2; ++t)
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) ka[t][kk] = k_operand(stg, sc, t, kk, n, j, g);
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) va[dt] = v_operand(stg, sc, dt, n, j, g);
-  const __bf16 one = (__bf16)1.0f;
-  const bf16x8 ones = {one, one, one, one, one, one, one, one};
+  const _Float16 one = (_Float16)1.0f;
+  const f16x8 ones = {one, one, one, one, one, one, one, one};
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
     if (c >= nc) break;   // uniform
     f32x4 s0 = st.negm[c], s1 = st.negm[c];
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[0][kk], qh[c][kk], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[1][kk], qh[c][kk], s1, 0, 0, 0);
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[0][kk], ql[c][kk], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[1][kk], ql[c][kk], s1, 0, 0, 0);
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[0][kk], qf[c][kk], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[1][kk], qf[c][kk], s1, 0, 0, 0);
     }
     block_tile(s0, s1, va, ones, u0, j, st, c);
   }
@@ -469,6 +486,32 @@ __device__ __forceinline__ void pack_q(const float (&y)[16], int half, float mul
     hi[i] = h[0]; hi[i + 1] = h[1];
     lo[i] = l[0]; lo[i + 1] = l[1];
   }
+}
+
+// Blocks: one K-step of the B operand of S^T in fp16, q[8j + i (+32)] * mul.
+__device__ __forceinline__ f16x8 pack_q16(const float (&y)[16], int half, float mul) {
+  f16x8 r;
+#pragma unroll
+  for (int i = 0; i < 8; i += 2) {
+    const f16x2 h = __builtin_convertvector((f32x2{y[8 * half + i] * mul, y[8 * half + i + 1] * mul}),
+                                            f16x2);
+    r[i] = h[0];
+    r[i + 1] = h[1];
+  }
+  return r;
+}
+
+// Blocks: the power-of-two exponent e >= 0 that keeps a column's |q| * qmul *
+// 2^-e below 2^15 (fp16 holds up to 65504); 0 for any ordinary input.
+__device__ __forceinline__ int q_exponent(const float (&y)[16], float qmul) {
+  float amax = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) amax = fmaxf(amax, fabsf(y[k] * qmul));
+  amax = head_max(amax);
+  if (!(amax >= 32768.0f) || amax == INFINITY) return 0;
+  int ex;
+  frexpf(amax, &ex);   // amax = f * 2^ex, f in [0.5, 1)
+  return ex - 15;
 }
 
 // Decode: head n's column of the block-diagonal Q^T.  K-step kk covers KV head
@@ -898,15 +941,17 @@ __device__ __forceinline__ void process_segment_block(const StepArgs &a, int b, 
   }
   store_table(a, tin, sh.lrows);
 
-  bf16x8 qh[2][2], ql[2][2];
+  f16x8 qf[2][2];
   BlockState st;
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
     const int tk = tok(c);
     float yq[16];
     q_values2(a, qin[c], wv, j, sh.cs[tk < nt ? tk : nt - 1], yq);
-    pack_q(yq, 0, qmul, qh[c][0], ql[c][0]);
-    pack_q(yq, 1, qmul, qh[c][1], ql[c][1]);
+    st.e[c] = q_exponent(yq, qmul);
+    const float mul = ldexpf(qmul, -st.e[c]);
+    qf[c][0] = pack_q16(yq, 0, mul);
+    qf[c][1] = pack_q16(yq, 1, mul);
     // causal bound: the token's position; window: 2047 keys before it
     const int p = cpos[c];
     st.hi[c] = tk < nt ? (p < r.khi ? p : r.khi) : -1;
@@ -916,6 +961,7 @@ __device__ __forceinline__ void process_segment_block(const StepArgs &a, int b, 
 #pragma unroll
     for (int dt = 0; dt < 5; ++dt) st.o[dt][c] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
+  st.scaled = __any(st.e[0] != 0 || st.e[1] != 0);
   if constexpr (VERIFY) {
     // the new rows: a workgroup release before the barrier orders the writes
     // before this work-group's own loads.  (Prefill rows come from rows_kernel.)
@@ -946,12 +992,12 @@ __device__ __forceinline__ void process_segment_block(const StepArgs &a, int b, 
       const Stage &sg = sh.stg[s & 1];
       if constexpr (VERIFY) {
         if (2 * s + cl < nch && nc > 0)
-          block_subchunk(sg, cl, kstart + (2 * s + cl) * CHUNK, lane, g, nc, qh, ql, st);
+          block_subchunk(sg, cl, kstart + (2 * s + cl) * CHUNK, lane, g, nc, qf, st);
       } else {
         if (nc > 0) {
-          block_subchunk(sg, 0, kstart + 2 * s * CHUNK, lane, g, nc, qh, ql, st);
+          block_subchunk(sg, 0, kstart + 2 * s * CHUNK, lane, g, nc, qf, st);
           if (2 * s + 1 < nch)
-            block_subchunk(sg, 1, kstart + (2 * s + 1) * CHUNK, lane, g, nc, qh, ql, st);
+            block_subchunk(sg, 1, kstart + (2 * s + 1) * CHUNK, lane, g, nc, qf, st);
         }
       }
     };

@@ -12,7 +12,8 @@ import paged_fp8_kv_amd as P
 from oracle import museattn_oracle as O
 from paged_fp8_kv_amd import workloads as W
 
-from gpu_common import full_check, gpu_new_bytes, log, new_rows, oracle_prologue, run, upload
+from gpu_common import (EPS, compare_out, full_check, gpu_new_bytes, log, new_rows,
+                        oracle_prologue, run, upload)
 
 pytestmark = pytest.mark.gpu
 
@@ -222,6 +223,46 @@ def test_value_encoder_exhaustive_over_bf16():
     _, vb_gpu = gpu_new_bytes(w, d)
     _, _, vb, _ = oracle_prologue(w)
     assert np.array_equal(vb_gpu, vb)
+
+
+@pytest.mark.parametrize("L", [1, 8, 40], ids=["decode", "verify", "prefill"])
+def test_q_beyond_half_precision_range(L):
+    """q_scale 1e6 puts |q| * log2(e)/8 far past 65504, the largest fp16
+    value the block path's q operand can hold: such a column is held as
+    q * 2^-e and its products are scaled back by 2^e.  The softmax is then a
+    hard argmax (scores of order 1e7 in log2 units), so the output of a
+    (token, head) is the gated norm of its best key's v.  Columns whose two
+    best keys lie closer than the fp16 rounding of q can move (2^14 log2
+    units) are left out: either key is a correct answer there."""
+    qs = 1.0e6
+    w = W.make(f"big-q-L{L}", 31, 2, L, 300, W.FULL, 1, 1.0)
+    host = W.build_pools_numpy(w)
+    d = upload(w)
+    P.attn_step(d["qkv"], d["positions"], d["table"], d["seq_lens"], d["k_cache"], d["v_cache"],
+                w.kv_scale, w.page_size, w.layer_kind, d["out"],
+                q_norm_w=d["w_q"], k_norm_w=d["w_k"], o_norm_w=d["w_o"],
+                max_seq_len=w.max_seq_len, eps=EPS, q_scale=qs, rope_base=10000.0)
+    torch.cuda.synchronize()
+    kb_gpu, vb_gpu = gpu_new_bytes(w, d)
+    kp, vp = host[0].copy(), host[1].copy()
+    want, _, _ = O.attn_step(w.qkv.float().numpy(), w.positions, w.table, kp, vp, B=w.B, L=w.L,
+                             page_size=1, layer_kind=W.FULL, kv_scale=1.0, w_q=w.w_q, w_k=w.w_k,
+                             w_o=w.w_o, eps=EPS, q_scale=qs, new_rows=(kb_gpu, vb_gpu))
+    # the gap between each column's two best scores (log2 units), from the
+    # pools the oracle attended to
+    q = O.prologue(w.qkv.float().numpy(), w.positions, w.w_q, w.w_k, eps=EPS, q_scale=qs,
+                   rope=False, rope_base=10000.0, kv_scale=1.0)[0]
+    keep = np.zeros((w.B, w.L, 16), bool)
+    for b in range(w.B):
+        for jt in range(w.L):
+            p = int(w.positions[b * w.L + jt])
+            kd = O.e4m3_decode(kp[O.cache_row(w.table, b, np.arange(p + 1), 1)])
+            for h in range(16):
+                sc = np.sort(kd[:, h // 8, :] @ q[b * w.L + jt, h] / 8.0 * np.log2(np.e))
+                keep[b, jt, h] = sc[-1] - sc[-2] > 2.0 ** 14
+    assert keep.mean() > 0.9
+    got = d["out"].float().cpu().numpy().reshape(w.B, w.L, 16, 64)[keep]
+    compare_out(got, want.reshape(w.B, w.L, 16, 64)[keep], f"{w.name} ({int(keep.sum())} columns)")
 
 
 def test_graph_capture_replays_match_eager():
