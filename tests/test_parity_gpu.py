@@ -146,6 +146,20 @@ def test_million_key_verify_block():
     full_check(w, d, requests=[0])
 
 
+def test_maximum_batch():
+    """1,024 requests, the most one call takes: the plan's prefix sums hold two
+    units per thread, and work-group shares cross many request boundaries."""
+    for L, kind in ((1, W.FULL), (2, W.SLIDING)):
+        w = W.make(f"max-batch-L{L}", 41, 1024, L, (1, 300), kind, 1, 1.0)
+        log(f"[edge] {w.name} work-groups={P.work_groups(w.B, L, w.max_seq_len, kind)}")
+        host = W.build_pools_numpy(w)
+        d = upload(w)
+        run(w, d)
+        torch.cuda.synchronize()
+        full_check(w, d, host_pools=host)
+        del d
+
+
 # ----------------------------------------------------------- properties
 
 def test_partition_invariance_and_determinism():

@@ -85,6 +85,20 @@ def test_prefill_full_size_sampled(case):
     torch.cuda.empty_cache()
 
 
+def test_prefill_at_the_unit_limit():
+    """4 requests x 16,384 block tokens = 4,096 plan units of 16 tokens, the
+    most one call takes; the oracle recomputes sampled tokens of every request."""
+    w = W.make("pf-max-units", 64, 4, 16384, (0, 100), W.FULL, 1, 1.0)
+    log(f"[prefill] {w.name} ctx={w.ctx.tolist()} units={w.B * 16384 // 16}")
+    d = upload(w)
+    run(w, d)
+    torch.cuda.synchronize()
+    full_check(w, d, tokens=[0, 15, 16, 8191, 16383])
+    assert torch.isfinite(d["out"].float()).all()
+    del d
+    torch.cuda.empty_cache()
+
+
 def test_prefill_partition_invariance():
     """The work-group count changes only the summation order."""
     w = W.make("pf-partition", 63, 2, 100, (1500, 2500), W.FULL, 1, 1.0)
