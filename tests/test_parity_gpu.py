@@ -279,8 +279,12 @@ def test_q_beyond_half_precision_range(L):
     compare_out(got, want.reshape(w.B, w.L, 16, 64)[keep], f"{w.name} ({int(keep.sum())} columns)")
 
 
-def test_graph_capture_replays_match_eager():
-    w = W.make("graph", 8, 4, 1, (2000, 5000), W.FULL, 1, 1.0)
+@pytest.mark.parametrize("L,kind", [(1, W.FULL), (8, W.SLIDING), (40, W.FULL)],
+                         ids=["decode", "verify", "prefill"])
+def test_graph_capture_replays_match_eager(L, kind):
+    """The step captured into a HIP graph (as a decode loop replays it) gives
+    the eager call's bytes on every replay, with eager calls in between."""
+    w = W.make(f"graph-L{L}", 8, 4, L, (2000, 5000), kind, 1, 1.0)
     d = upload(w)
     ws = torch.empty(P.workspace_bytes(w.B, w.L, w.max_seq_len, w.page_size, w.layer_kind),
                      dtype=torch.uint8, device="cuda:0")
