@@ -179,7 +179,13 @@ int museattn_attn_step_profiled(const void *qkv, const int32_t *positions, const
   a.work_groups = ly.work_groups;
   // a segment start-up (batch of loads + first rows) is worth about this many
   // 32-key chunks of one work-group's streaming (measured on MI355X)
-  a.seg_cost = L == 1 ? 14 : (L <= 8 ? 4 : 2);
+#ifndef MUSEATTN_SEG_COST_VERIFY
+#define MUSEATTN_SEG_COST_VERIFY 16
+#endif
+#ifndef MUSEATTN_SEG_COST_PREFILL
+#define MUSEATTN_SEG_COST_PREFILL 16
+#endif
+  a.seg_cost = L == 1 ? 14 : (L <= 8 ? MUSEATTN_SEG_COST_VERIFY : MUSEATTN_SEG_COST_PREFILL);
   a.tb = unit_tokens(L);
   a.nblk = units_per_request(L);
   a.nunits = B * a.nblk;
