@@ -27,9 +27,10 @@
 // One 8-wave work-group per CU: two work-groups sharing a CU progress at
 // unequal rates (the older one wins issue arbitration), so the younger one
 // would finish alone.  Decode (L = 1): the 8 waves take interleaved chunks of
-// a segment and merge their states in LDS.  Verify (L >= 2): the 8 tokens x 8
-// heads of a KV group form a dense 64-column contraction (see the verify
-// section below); waves split the KV heads, the column tiles and the chunks.
+// a segment and merge their states in LDS.  Verify and prefill blocks (L >=
+// 2): the block tokens x 8 heads of a KV group form a dense contraction on
+// fp16 MFMA over K/V staged in LDS (see the block section below); waves split
+// the KV heads, the column tiles and (verify) the sub-chunks.
 #include "device_common.h"
 #include "launch.h"
 
@@ -218,9 +219,9 @@ __device__ __forceinline__ void compute_chunk(const RowBuf &rb, int u0, int lane
 // 32-key sub-chunks) that its 8 waves share:
 //  * staging: thread t loads 32 B of key t/8's K row (t%8 < 4) or V row
 //    (t%8 >= 4), so 4 lanes read one whole 128-B row; the bytes are converted
-//    to fp16 (exactly) once for the work-group and written, key-major, into one of two
-//    LDS stage buffers (rows padded against bank conflicts).  The loads run
-//    BLOCK_PREFETCH steps ahead in registers; one barrier per step.
+//    to fp16 (exactly) once for the work-group and written, key-major, into
+//    one of two LDS stage buffers (rows padded against bank conflicts).  The
+//    loads run BLOCK_PREFETCH steps ahead in registers; one barrier per step.
 //  * S^T (32 keys x 16 columns) per sub-chunk and column tile: 2 key tiles x
 //    2 K-steps of v_mfma_f32_16x16x32_f16; A = K rows from LDS (K-step kk:
 //    dims 32kk + 8j..+7 in lane (n, j)), B = Q^T from registers in fp16 (11
