@@ -30,9 +30,13 @@ def _need_gpu():
     P.lib()
 
 
-@pytest.mark.parametrize("T,hidden", [(1, 64), (7, 8192), (32, 8192), (33, 1088), (100, 2048),
-                                      (256, 8192)])
+@pytest.mark.parametrize("T,hidden", [(1, 64), (7, 8192), (32, 8192), (33, 1088), (64, 8192),
+                                      (65, 64), (100, 2048), (129, 1088), (256, 8192),
+                                      (753, 8192)])
 def test_oproj_alone(T, hidden):
+    """T <= 64 runs the register kernel, larger T the LDS-tiled one (128 x 128
+    tiles: hidden 64 and 1088 leave a partial row tile, T 65, 129 and 753 a
+    partial token tile)."""
     a = W.oproj_input(70 + T, T)
     o = W.oproj_weight(71, hidden)
     y = torch.empty(T, hidden, dtype=torch.bfloat16, device="cuda")
