@@ -378,7 +378,9 @@ __device__ __forceinline__ void block_tile(f32x4 s0, f32x4 s1, const f16x8 (&va)
       alpha = 1.0f;
       st.m[c] = cm;
     } else {
-      d = fmaxf(cm, 0.0f);
+      // only a column past the slack moves: the branch is taken for the whole
+      // wave, and a column's numbers must not depend on its neighbours'
+      d = cm > RESCALE_SLACK ? cm : 0.0f;
       alpha = __builtin_amdgcn_exp2f(-d);
       st.m[c] += d;
     }

@@ -209,6 +209,47 @@ def test_many_requests_sharing_work_groups():
         full_check(w, d, host_pools=host)
 
 
+@pytest.mark.parametrize("L,kind", [(8, W.FULL), (5, W.SLIDING), (40, W.FULL)],
+                         ids=["verify-full", "verify-sliding", "prefill"])
+def test_causal_in_block(L, kind):
+    """Changing the last block token's row (its q, k, v and gate) leaves every
+    earlier token's output bitwise unchanged: none of them sees its key."""
+    w = W.make(f"causal-L{L}", 17, 3, L, (1500, 3000), kind, 1, 1.0)
+    d = upload(w)
+    run(w, d)
+    torch.cuda.synchronize()
+    before = d["out"].clone()
+    g = torch.Generator().manual_seed(5)
+    last = torch.arange(w.B) * L + (L - 1)
+    d["qkv"][last] = torch.randn(w.B, d["qkv"].shape[1], generator=g).to(torch.bfloat16).cuda()
+    run(w, d)
+    torch.cuda.synchronize()
+    assert torch.equal(d["out"][:, :L - 1], before[:, :L - 1])
+    assert not torch.equal(d["out"][:, L - 1], before[:, L - 1])
+
+
+@pytest.mark.parametrize("L", [1, 8], ids=["decode", "verify"])
+def test_requests_are_independent(L):
+    """Request 2's inputs and cached rows changed: the other requests' outputs
+    stay bitwise the same (work-group shares that span two requests keep
+    separate states per request)."""
+    w = W.make(f"indep-L{L}", 18, 4, L, (3000, 6000), W.FULL, 1, 1.0)
+    d = upload(w)
+    run(w, d, work_groups=7)   # shares cross request boundaries
+    torch.cuda.synchronize()
+    before = d["out"].clone()
+    g = torch.Generator().manual_seed(6)
+    d["qkv"][2 * L:3 * L] = torch.randn(L, d["qkv"].shape[1], generator=g).to(torch.bfloat16).cuda()
+    rows = torch.from_numpy(w.table[2, :int(w.ctx[2])].astype(np.int64)).cuda()
+    d["k_cache"][rows] = torch.randint(0, 0x7e, (rows.numel(), 2, 64), generator=g,
+                                       dtype=torch.uint8).cuda()
+    run(w, d, work_groups=7)
+    torch.cuda.synchronize()
+    keep = [0, 1, 3]
+    assert torch.equal(d["out"][keep], before[keep])
+    assert not torch.equal(d["out"][2], before[2])
+
+
 def test_page_size_does_not_change_the_result():
     outs = []
     for ps in (1, 64):
