@@ -281,6 +281,32 @@ def test_value_encoder_exhaustive_over_bf16():
 
 
 @pytest.mark.parametrize("L", [1, 8, 40], ids=["decode", "verify", "prefill"])
+def test_other_norm_and_rope_parameters(L):
+    """eps, q_scale and rope_base reach every kernel: eps 1e-5, q_scale 1 and
+    rope base 500,000 on a sliding layer, 64-token pages, kv_scale 1/64."""
+    eps, qs, base = float(np.float32(1e-5)), 1.0, 500000.0
+    w = W.make(f"params-L{L}", 32, 2, L, (2500, 4000), W.SLIDING, 64, 1.0 / 64)
+    host = W.build_pools_numpy(w)
+    d = upload(w)
+    P.attn_step(d["qkv"], d["positions"], d["table"], d["seq_lens"], d["k_cache"], d["v_cache"],
+                w.kv_scale, w.page_size, w.layer_kind, d["out"],
+                q_norm_w=d["w_q"], k_norm_w=d["w_k"], o_norm_w=d["w_o"],
+                max_seq_len=w.max_seq_len, eps=eps, q_scale=qs, rope_base=base)
+    torch.cuda.synchronize()
+    kb_gpu, vb_gpu = gpu_new_bytes(w, d)
+    _, kb, vb, _ = O.prologue(w.qkv.float().numpy(), w.positions, w.w_q, w.w_k, eps=eps,
+                              q_scale=qs, rope=True, rope_base=base, kv_scale=w.kv_scale)
+    assert np.abs(O.e4m3_ordinal(kb_gpu) - O.e4m3_ordinal(kb)).max() <= 1
+    assert np.array_equal(vb_gpu, vb)
+    want, _, _ = O.attn_step(w.qkv.float().numpy(), w.positions, w.table, host[0].copy(),
+                             host[1].copy(), B=w.B, L=w.L, page_size=w.page_size,
+                             layer_kind=w.layer_kind, kv_scale=w.kv_scale, w_q=w.w_q, w_k=w.w_k,
+                             w_o=w.w_o, eps=eps, q_scale=qs, rope_base=base,
+                             new_rows=(kb_gpu, vb_gpu))
+    compare_out(d["out"].float().cpu().numpy(), want, w.name)
+
+
+@pytest.mark.parametrize("L", [1, 8, 40], ids=["decode", "verify", "prefill"])
 def test_q_beyond_half_precision_range(L):
     """q_scale 1e6 puts |q| * log2(e)/8 far past 65504, the largest fp16
     value the block path's q operand can hold: such a column is held as
