@@ -37,8 +37,9 @@
  *  - the library never allocates, frees, synchronises or reads device values
  *    on the host; all work is enqueued on `stream`, so a call can be captured
  *    into a HIP graph.  Nothing is cached between calls.
- *  - k_cache / v_cache are written only at the B*L new rows; `out` must not
- *    overlap `qkv`; `workspace` holds scratch data of one call (it must not be
+ *  - k_cache / v_cache are written only at the B*L new rows.  qkv, out,
+ *    k_cache, v_cache (num_rows rows each) and workspace must not overlap
+ *    one another; `workspace` holds scratch data of one call (it must not be
  *    shared by calls that may run concurrently).
  *  - device-side indices are clamped into the extents the host validated
  *    (rows into [0, num_rows), positions into [0, max_seq_len)), so
@@ -89,7 +90,7 @@ enum museattn_status {
                                      or not 256-byte aligned */
   MUSEATTN_ERR_PARAM = -8,        /* kv_scale, eps, q_scale, rope_base or
                                      work_groups out of range */
-  MUSEATTN_ERR_ALIAS = -9,        /* out overlaps qkv */
+  MUSEATTN_ERR_ALIAS = -9,        /* two of qkv, out, k_cache, v_cache, workspace overlap */
   MUSEATTN_ERR_LAUNCH = -10       /* a kernel launch failed */
 };
 

@@ -82,7 +82,7 @@ const char *museattn_strerror(int status) {
     case MUSEATTN_ERR_ALIGN: return "misaligned pointer (caches, qkv and weights need 16 bytes, out 8)";
     case MUSEATTN_ERR_WORKSPACE: return "workspace too small or not 256-byte aligned";
     case MUSEATTN_ERR_PARAM: return "kv_scale, eps, q_scale, rope_base or work_groups out of range";
-    case MUSEATTN_ERR_ALIAS: return "out overlaps qkv";
+    case MUSEATTN_ERR_ALIAS: return "buffers overlap (qkv, out, k_cache, v_cache, workspace)";
     case MUSEATTN_ERR_LAUNCH: return "kernel launch failed";
     default: return "unknown status";
   }
@@ -128,9 +128,22 @@ int museattn_check_args(const void *qkv, const int32_t *positions, const int32_t
   if (!aligned(workspace, 256) ||
       workspace_bytes < museattn_workspace_bytes(B, L, max_seq_len, page_size, layer_kind, params))
     return MUSEATTN_ERR_WORKSPACE;
-  const uintptr_t q0 = (uintptr_t)qkv, q1 = q0 + (uintptr_t)B * L * QKV_W * 2;
-  const uintptr_t o0 = (uintptr_t)out, o1 = o0 + (uintptr_t)B * L * HQ * D * 2;
-  if (o0 < q1 && q0 < o1) return MUSEATTN_ERR_ALIAS;
+  // the buffers the step writes (out, the caches' new rows, the workspace)
+  // must not overlap what it reads or each other
+  struct Span {
+    uintptr_t lo, hi;
+  };
+  auto span = [](const void *p, uint64_t bytes) {
+    return Span{(uintptr_t)p, (uintptr_t)p + (uintptr_t)bytes};
+  };
+  auto meet = [](Span x, Span y) { return x.lo < y.hi && y.lo < x.hi; };
+  const uint64_t T = (uint64_t)B * L;
+  const Span sq = span(qkv, T * QKV_W * 2), so = span(out, T * HQ * D * 2);
+  const Span sk = span(k_cache, (uint64_t)num_rows * ROW), sv = span(v_cache, (uint64_t)num_rows * ROW);
+  const Span sw = span(workspace, workspace_bytes);
+  if (meet(so, sq) || meet(so, sk) || meet(so, sv) || meet(so, sw) || meet(sw, sq) ||
+      meet(sw, sk) || meet(sw, sv) || meet(sk, sv) || meet(sk, sq) || meet(sv, sq))
+    return MUSEATTN_ERR_ALIAS;
   return MUSEATTN_OK;
 }
 

@@ -101,6 +101,10 @@ def test_valid_arguments_pass():
     (dict(work_groups=65536), -8),
     (dict(B=1025), -4),
     (dict(out=A["qkv"] + 4096), -9),
+    (dict(out=A["kc"] + 4096), -9),          # out inside the K cache
+    (dict(ws=A["vc"] + 1024), -9),           # workspace inside the V cache
+    (dict(ws=A["out"]), -9),                 # workspace over out
+    (dict(kc=A["vc"]), -9),                  # one array for both caches
 ])
 def test_invalid_arguments_are_rejected(kw, status):
     assert _check(**kw) == status
