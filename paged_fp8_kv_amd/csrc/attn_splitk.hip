@@ -846,7 +846,7 @@ __device__ __forceinline__ void q_values2(const StepArgs &a, const QIn2 &in, con
 }
 
 #ifndef MUSEATTN_BLOCK_PREFETCH
-#define MUSEATTN_BLOCK_PREFETCH 3
+#define MUSEATTN_BLOCK_PREFETCH 2
 #endif
 
 // One segment of a verify (MODE 2) or prefill (MODE 3) block: chunks [x, y)
