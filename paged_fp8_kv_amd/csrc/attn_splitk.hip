@@ -38,7 +38,9 @@ namespace museattn {
 
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr int MAX_SPLIT_LDS = 4096;   // table entries cached per work-group
-constexpr float RESCALE_SLACK = 8.0f;  // log2 units a stale reference max may lag
+// log2 units a stale reference max may lag: P <= 2^15 stays inside fp16's
+// range (65504) in the block products
+constexpr float RESCALE_SLACK = 15.0f;
 
 struct RowBuf {
   uint4 k[4];   // [tile*2 + kv head] 16 B of K row
