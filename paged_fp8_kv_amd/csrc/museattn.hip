@@ -198,7 +198,11 @@ int museattn_attn_step_profiled(const void *qkv, const int32_t *positions, const
 #ifndef MUSEATTN_SEG_COST_PREFILL
 #define MUSEATTN_SEG_COST_PREFILL 16
 #endif
-  a.seg_cost = L == 1 ? 14 : (L <= 8 ? MUSEATTN_SEG_COST_VERIFY : MUSEATTN_SEG_COST_PREFILL);
+#ifndef MUSEATTN_SEG_COST_DECODE
+#define MUSEATTN_SEG_COST_DECODE 14
+#endif
+  a.seg_cost = L == 1 ? MUSEATTN_SEG_COST_DECODE
+                      : (L <= 8 ? MUSEATTN_SEG_COST_VERIFY : MUSEATTN_SEG_COST_PREFILL);
   a.tb = unit_tokens(L);
   a.nblk = units_per_request(L);
   a.nunits = B * a.nblk;
