@@ -1163,11 +1163,13 @@ __global__ __launch_bounds__(THREADS, 2) void attn_kernel(StepArgs a) {
   }
   __syncthreads();
   // Cost space: unit u occupies seg_cost units (its segment start-up, in
-  // chunk-equivalents) followed by its chunks, so unit u starts at cost
-  // Q_u = pref[u] + u * seg_cost.  Work-groups take equal cost shares; one
-  // whose share covers a unit start gets correspondingly fewer chunks.
-  const int pen = a.seg_cost;
-  const int64_t Ct = (int64_t)sh.pref[NU] + (int64_t)NU * pen;
+  // chunk-equivalents), then its chunks, then end_cost units (the new rows
+  // the holder of its last chunk writes), so unit u starts at cost Q_u =
+  // pref[u] + u * (seg_cost + end_cost).  Work-groups take equal cost
+  // shares; one whose share covers a unit's start or end gets
+  // correspondingly fewer chunks.
+  const int pen = a.seg_cost, per = a.seg_cost + a.end_cost;
+  const int64_t Ct = (int64_t)sh.pref[NU] + (int64_t)NU * per;
   const int w = blockIdx.x;
   const int G = Ct < a.work_groups ? (int)Ct : a.work_groups;
   if (w == 0) {
@@ -1177,7 +1179,7 @@ __global__ __launch_bounds__(THREADS, 2) void attn_kernel(StepArgs a) {
   }
   if (w >= G) return;   // uniform over the work-group
   const int64_t cb = (int64_t)w * Ct / G, ce = (int64_t)(w + 1) * Ct / G;
-  auto cost_of = [&](int uu) { return (int64_t)sh.pref[uu] + (int64_t)uu * pen; };
+  auto cost_of = [&](int uu) { return (int64_t)sh.pref[uu] + (int64_t)uu * per; };
   int u = 0;
   {
     int hi = NU - 1;

@@ -31,14 +31,15 @@ __global__ __launch_bounds__(256) void combine_kernel(StepArgs a) {
   const int u = b * a.nblk + blk, NU = a.nunits;
   const int64_t p0 = a.plan[u], p1 = a.plan[u + 1];
   const int G = a.plan[NU + 1];
-  const int64_t Ct = (int64_t)a.plan[NU] + (int64_t)NU * a.seg_cost;
+  const int64_t Ct = (int64_t)a.plan[NU] + (int64_t)NU * (a.seg_cost + a.end_cost);
   const float g = bf16_bits_to_f32(a.qkv[(size_t)t * QKV_W + G_OFF + h * D + lane]);
   const float wo = a.wo[lane];
   // slots of unit u: w + u for the work-groups w whose cost share meets its
-  // chunks (chunk c of unit u sits at cost p0 + (u + 1) * seg_cost + c)
+  // chunks (chunk c of unit u sits at cost p0 + u (seg_cost + end_cost) +
+  // seg_cost + c)
   int s0 = 0, s1 = -1;
   if (p1 > p0) {
-    const int64_t q0 = p0 + (int64_t)(u + 1) * a.seg_cost;
+    const int64_t q0 = p0 + (int64_t)u * (a.seg_cost + a.end_cost) + a.seg_cost;
     s0 = wg_of_chunk(q0, Ct, G) + u;
     s1 = wg_of_chunk(q0 + (p1 - p0) - 1, Ct, G) + u;
   }
@@ -114,13 +115,13 @@ __global__ __launch_bounds__(256) void combine_tokens_kernel(StepArgs a) {
   const int u = b * a.nblk + blk, NU = a.nunits;
   const int64_t p0 = a.plan[u], p1 = a.plan[u + 1];
   const int G = a.plan[NU + 1];
-  const int64_t Ct = (int64_t)a.plan[NU] + (int64_t)NU * a.seg_cost;
+  const int64_t Ct = (int64_t)a.plan[NU] + (int64_t)NU * (a.seg_cost + a.end_cost);
   const uint2 graw = *reinterpret_cast<const uint2 *>(a.qkv + (size_t)t * QKV_W + G_OFF + h * D +
                                                       4 * dq);
   const f32x4 wo = *reinterpret_cast<const f32x4 *>(a.wo + 4 * dq);
   int s0 = 0, s1 = -1;
   if (p1 > p0) {
-    const int64_t q0 = p0 + (int64_t)(u + 1) * a.seg_cost;
+    const int64_t q0 = p0 + (int64_t)u * (a.seg_cost + a.end_cost) + a.seg_cost;
     s0 = wg_of_chunk(q0, Ct, G) + u;
     s1 = wg_of_chunk(q0 + (p1 - p0) - 1, Ct, G) + u;
   }

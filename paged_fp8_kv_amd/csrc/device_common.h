@@ -50,6 +50,7 @@ struct StepArgs {
   int work_groups;         // attention work-groups launched (each takes an equal
                            // share of all requests' key chunks)
   int seg_cost;            // chunk-equivalents one segment start-up costs
+  int end_cost;            // and the unit's end (verify: its new rows)
   // Plan units: request b's block tokens in groups of tb (unit u = b * nblk +
   // blk holds tokens blk*tb ..); one group per request (tb = L) up to L = 8.
   int tb, nblk, nunits;

@@ -203,6 +203,15 @@ int museattn_attn_step_profiled(const void *qkv, const int32_t *positions, const
 #endif
   a.seg_cost = L == 1 ? MUSEATTN_SEG_COST_DECODE
                       : (L <= 8 ? MUSEATTN_SEG_COST_VERIFY : MUSEATTN_SEG_COST_PREFILL);
+#ifndef MUSEATTN_END_COST_DECODE
+#define MUSEATTN_END_COST_DECODE 0
+#endif
+#ifndef MUSEATTN_END_COST_VERIFY
+#define MUSEATTN_END_COST_VERIFY 8
+#endif
+  // the work-group holding a unit's last chunk also writes its new rows
+  // (prefill rows are written by their own kernel)
+  a.end_cost = L == 1 ? MUSEATTN_END_COST_DECODE : (L <= 8 ? MUSEATTN_END_COST_VERIFY : 0);
   a.tb = unit_tokens(L);
   a.nblk = units_per_request(L);
   a.nunits = B * a.nblk;
