@@ -173,8 +173,15 @@ __global__ __launch_bounds__(256) void combine_tokens_kernel(StepArgs a) {
       uint2{packed[0], packed[1]};
 }
 
+#ifndef MUSEATTN_TOKENS_COMBINE_MIN_B
+#define MUSEATTN_TOKENS_COMBINE_MIN_B 24
+#endif
+#ifndef MUSEATTN_TOKENS_COMBINE_MIN_L
+#define MUSEATTN_TOKENS_COMBINE_MIN_L 2
+#endif
+
 void launch_combine(const StepArgs &a, hipStream_t stream) {
-  if (a.L > 8)
+  if (a.L > 8 || (a.L >= MUSEATTN_TOKENS_COMBINE_MIN_L && a.B >= MUSEATTN_TOKENS_COMBINE_MIN_B))
     hipLaunchKernelGGL(combine_tokens_kernel, dim3(a.B * a.L), dim3(256), 0, stream, a);
   else
     hipLaunchKernelGGL(combine_kernel, dim3(a.B * a.L * HQ), dim3(256), 0, stream, a);
