@@ -18,6 +18,9 @@
 
 namespace museattn {
 
+// KB > 0: each slot lane loads its first KB slots in one batch (for units with
+// many slots: one long request spread over every work-group).
+template <int KB>
 __global__ __launch_bounds__(256) void combine_kernel(StepArgs a) {
   __shared__ float sm_m[16], sm_l[16];
   __shared__ __attribute__((aligned(16))) float sm_o[16][D];
@@ -60,6 +63,32 @@ __global__ __launch_bounds__(256) void combine_kernel(StepArgs a) {
     m = mn;
   };
   int s = s0 + sl;
+  if constexpr (KB > 0) {
+    float2 v[KB];
+    f32x4 x[KB];
+#pragma unroll
+    for (int k = 0; k < KB; ++k) {
+      const int sk = s + 16 * k;
+      v[k] = float2{-INFINITY, 0.0f};
+      x[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (sk <= s1) {
+        const size_t e = entry(sk);
+        v[k] = ml[e];
+        x[k] = po[e * (D / 4) + dq];
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < KB; ++k) m = fmaxf(m, v[k].x);
+    if (m != -INFINITY) {
+#pragma unroll
+      for (int k = 0; k < KB; ++k) {
+        const float c = v[k].x == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(v[k].x - m);
+        l += v[k].y * c;
+        o += x[k] * c;
+      }
+    }
+    s += 16 * KB;
+  }
   for (; s + 48 <= s1; s += 64) {
     float2 v[4];
     f32x4 x[4];
@@ -176,15 +205,27 @@ __global__ __launch_bounds__(256) void combine_tokens_kernel(StepArgs a) {
 #ifndef MUSEATTN_TOKENS_COMBINE_MIN_B
 #define MUSEATTN_TOKENS_COMBINE_MIN_B 24
 #endif
+#ifndef MUSEATTN_COMBINE_BATCH_SLOTS
+#define MUSEATTN_COMBINE_BATCH_SLOTS 48
+#endif
 #ifndef MUSEATTN_TOKENS_COMBINE_MIN_L
 #define MUSEATTN_TOKENS_COMBINE_MIN_L 2
 #endif
 
 void launch_combine(const StepArgs &a, hipStream_t stream) {
-  if (a.L > 8 || (a.L >= MUSEATTN_TOKENS_COMBINE_MIN_L && a.B >= MUSEATTN_TOKENS_COMBINE_MIN_B))
+  if (a.L > 8 || (a.L >= MUSEATTN_TOKENS_COMBINE_MIN_L && a.B >= MUSEATTN_TOKENS_COMBINE_MIN_B)) {
     hipLaunchKernelGGL(combine_tokens_kernel, dim3(a.B * a.L), dim3(256), 0, stream, a);
+    return;
+  }
+  // one request over many work-groups leaves many slots per unit: at most
+  // one per work-group, and no more than its chunks (plus start-up) allow
+  const int64_t chunks = ((int64_t)a.max_seq_len + CHUNK - 1) / CHUNK + a.seg_cost + a.end_cost;
+  const int64_t slots = a.B == 1 ? (chunks < a.work_groups ? chunks : a.work_groups)
+                                 : a.work_groups / a.B + 2;
+  if (slots > MUSEATTN_COMBINE_BATCH_SLOTS)
+    hipLaunchKernelGGL(combine_kernel<16>, dim3(a.B * a.L * HQ), dim3(256), 0, stream, a);
   else
-    hipLaunchKernelGGL(combine_kernel, dim3(a.B * a.L * HQ), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(combine_kernel<0>, dim3(a.B * a.L * HQ), dim3(256), 0, stream, a);
 }
 
 }  // namespace museattn
