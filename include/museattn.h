@@ -185,7 +185,8 @@ int museattn_oproj(const void *a, const void *o_weight, int T, int hidden, void 
  * stream (the step's `out` still receives the gated output; the projection
  * reads it back from the cache hierarchy).  The two optional caller-created
  * hipEvent_t are recorded around the projection kernel.  Checks both calls'
- * arguments before enqueuing anything (y must also not overlap qkv). */
+ * arguments before enqueuing anything (y must also not overlap qkv, the
+ * caches or the workspace). */
 int museattn_attn_step_oproj(const void *qkv, const int32_t *positions, const int32_t *table,
                              const int32_t *seq_lens, void *k_cache, void *v_cache, float kv_scale,
                              int page_size, int layer_kind, void *out, void *stream, int B, int L,

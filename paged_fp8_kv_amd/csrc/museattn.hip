@@ -275,9 +275,18 @@ int museattn_attn_step_oproj(const void *qkv, const int32_t *positions, const in
   const int T = B * L;
   st = check_oproj(out, o_weight, T, hidden, y);
   if (st != MUSEATTN_OK) return st;
+  // y is written after the step: it must not overlap what the step reads or
+  // writes either
   const uintptr_t y0 = (uintptr_t)y, y1 = y0 + (uintptr_t)T * hidden * 2;
-  const uintptr_t q0 = (uintptr_t)qkv, q1 = q0 + (uintptr_t)T * MUSEATTN_QKV_WIDTH * 2;
-  if (y0 < q1 && q0 < y1) return MUSEATTN_ERR_ALIAS;
+  auto meets_y = [&](const void *p, uint64_t bytes) {
+    const uintptr_t p0 = (uintptr_t)p, p1 = p0 + (uintptr_t)bytes;
+    return y0 < p1 && p0 < y1;
+  };
+  if (meets_y(qkv, (uint64_t)T * MUSEATTN_QKV_WIDTH * 2) ||
+      meets_y(k_cache, (uint64_t)num_rows * MUSEATTN_ROW_BYTES) ||
+      meets_y(v_cache, (uint64_t)num_rows * MUSEATTN_ROW_BYTES) ||
+      meets_y(workspace, workspace_bytes))
+    return MUSEATTN_ERR_ALIAS;
   st = museattn_attn_step(qkv, positions, table, seq_lens, k_cache, v_cache, kv_scale, page_size,
                           layer_kind, out, stream, B, L, table_stride, max_seq_len, num_rows,
                           params, workspace, workspace_bytes);

@@ -153,3 +153,19 @@ def test_oproj_invalid_arguments_are_rejected(kw, status):
     args.update(kw)
     st = lib.museattn_oproj(args["a"], args["o"], args["T"], args["hidden"], args["y"], None)
     assert st == status
+
+
+@pytest.mark.parametrize("y_at,status", [("ws", -9), ("kc", -9), ("qkv", -9), ("wk", 0)])
+def test_step_oproj_output_must_not_overlap(y_at, status):
+    """museattn_attn_step_oproj: y may not overlap qkv, the caches or the
+    workspace (host checks only; an invalid call enqueues nothing, and the
+    valid one is not run: the check order is probed with a null o_weight)."""
+    lib = P.lib()
+    kw = _args()
+    o_w = 0 if status == 0 else A["wq"] + (1 << 30)
+    st = lib.museattn_attn_step_oproj(
+        kw["qkv"], kw["positions"], kw["table"], kw["seq_lens"], kw["k_cache"], kw["v_cache"],
+        kw["kv_scale"], kw["page_size"], kw["layer_kind"], kw["out"], None, kw["B"], kw["L"],
+        kw["table_stride"], kw["max_seq_len"], kw["num_rows"], ctypes.byref(kw["params"]),
+        kw["workspace"], kw["workspace_nbytes"], o_w, 8192, A[y_at] + 4096, None, None)
+    assert st == (status if status else -1)
