@@ -256,9 +256,13 @@ struct BlockState {
   f32x4 negm[2];   // -m (0 while m = -inf), the accumulator the scores start from
   float m[2];      // the column's reference max (log2 units)
   int lo[2], hi[2];   // visible key range of the lane column's token, inclusive
+  int ulo[2], uhi[2]; // wave-uniform: keys [ulo, uhi] are visible to every live column
+  float thr[2];       // the reference moves once the tile max passes this:
+                      // -inf while the column has no reference, else the slack
   int e[2];           // q of the lane column is held as q * 2^-e in fp16 (e = 0
                       // unless |q| * qmul reaches 2^15)
   bool scaled;        // some column of the wave has e > 0 (wave-uniform)
+  f16x8 ones;         // the all-ones operand of the P-sum tile
 };
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -357,22 +361,23 @@ __device__ __forceinline__ void block_tile(f32x4 s0, f32x4 s1, const f16x8 (&va)
 #pragma unroll
     for (int i = 0; i < 8; ++i) sc[i] = ldexpf(sc[i], st.e[c]);
   }
-  const int lo = st.lo[c], hi = st.hi[c];
-  if (u0 < lo || u0 + CHUNK - 1 > hi) {
+  if (u0 < st.ulo[c] || u0 + CHUNK - 1 > st.uhi[c]) {   // uniform
     // score i is key u0 + 4j + off_i, off_i = 16 (i / 4) + i % 4
-    const int elo = lo - u0 - 4 * j, ehi = hi - u0 - 4 * j;
+    const int elo = st.lo[c] - u0 - 4 * j, ehi = st.hi[c] - u0 - 4 * j;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int off = (i >> 2) * 16 + (i & 3);
       if (off < elo || off > ehi) sc[i] = -INFINITY;
     }
   }
-  const float lmax = fmax_ieee(fmax_ieee(fmax_ieee(sc[0], sc[1]), fmax_ieee(sc[2], sc[3])),
-                               fmax_ieee(fmax_ieee(sc[4], sc[5]), fmax_ieee(sc[6], sc[7])));
+  // four 3-input maxima
+  const float m01 = fmax_ieee(fmax_ieee(sc[0], sc[1]), sc[2]);
+  const float m23 = fmax_ieee(fmax_ieee(sc[3], sc[4]), sc[5]);
+  const float lmax = fmax_ieee(fmax_ieee(sc[6], sc[7]), fmax_ieee(m01, m23));
   // Lazy reference max: it moves only when a score passes it by more than
   // RESCALE_SLACK (so P <= 2^SLACK), or for the column's first visible keys.
-  const bool fresh = st.m[c] == -INFINITY;
-  if (__any(lmax > RESCALE_SLACK || (fresh && lmax != -INFINITY))) {
+  if (__any(lmax > st.thr[c])) {
+    const bool fresh = st.m[c] == -INFINITY;
     const float cm = head_max(lmax);   // the column's max, relative (or raw if fresh)
     float d, alpha;
     if (fresh) {
@@ -392,6 +397,7 @@ __device__ __forceinline__ void block_tile(f32x4 s0, f32x4 s1, const f16x8 (&va)
     for (int dt = 0; dt < 5; ++dt) st.o[dt][c] *= alpha;
     const float nm = st.m[c] == -INFINITY ? 0.0f : ldexpf(-st.m[c], -st.e[c]);
     st.negm[c] = f32x4{nm, nm, nm, nm};
+    st.thr[c] = st.m[c] == -INFINITY ? -INFINITY : RESCALE_SLACK;
   }
   float pv[8];
 #pragma unroll
@@ -420,8 +426,6 @@ __device__ __forceinline__ void block_subchunk(const Stage &stg, int sc, int u0,
     for (int kk = 0; kk < 2; ++kk) ka[t][kk] = k_operand(stg, sc, t, kk, n, j, g);
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) va[dt] = v_operand(stg, sc, dt, n, j, g);
-  const _Float16 one = (_Float16)1.0f;
-  const f16x8 ones = {one, one, one, one, one, one, one, one};
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
     if (c >= nc) break;   // uniform
@@ -431,7 +435,7 @@ __device__ __forceinline__ void block_subchunk(const Stage &stg, int sc, int u0,
       s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[0][kk], qf[c][kk], s0, 0, 0, 0);
       s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[1][kk], qf[c][kk], s1, 0, 0, 0);
     }
-    block_tile(s0, s1, va, ones, u0, j, st, c);
+    block_tile(s0, s1, va, st.ones, u0, j, st, c);
   }
 }
 
@@ -961,12 +965,31 @@ __device__ __forceinline__ void process_segment_block(const StepArgs &a, int b, 
     const int p = cpos[c];
     st.hi[c] = tk < nt ? (p < r.khi ? p : r.khi) : -1;
     st.lo[c] = a.sliding ? p - (WINDOW - 1) : 0;
+    // The columns' common visible range.  A tile's columns belong to two
+    // tokens, held by lanes 0 and 8; a dead token (its results are never
+    // written) does not narrow it.
+    {
+      const int lo0 = __builtin_amdgcn_readlane(st.lo[c], 0), lo1 = __builtin_amdgcn_readlane(st.lo[c], 8);
+      const int hi0 = __builtin_amdgcn_readlane(st.hi[c], 0), hi1 = __builtin_amdgcn_readlane(st.hi[c], 8);
+      const bool live1 = tok(c) - (n >> 3) + 1 < nt;   // uniform: the tile's second token
+      st.ulo[c] = live1 ? (lo0 > lo1 ? lo0 : lo1) : lo0;
+      st.uhi[c] = live1 ? (hi0 < hi1 ? hi0 : hi1) : hi0;
+    }
+    st.thr[c] = -INFINITY;
     st.m[c] = -INFINITY;
     st.negm[c] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int dt = 0; dt < 5; ++dt) st.o[dt][c] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   st.scaled = __any(st.e[0] != 0 || st.e[1] != 0);
+  {
+    // made opaque to the compiler, so that it keeps the operand in registers
+    // instead of rebuilding it with moves at every tile
+    uint32_t w[4] = {0x3c003c00u, 0x3c003c00u, 0x3c003c00u, 0x3c003c00u};   // fp16 1.0 pairs
+#pragma unroll
+    for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(w[i]));
+    st.ones = __builtin_bit_cast(f16x8, w);
+  }
   if constexpr (VERIFY) {
     // the new rows: a workgroup release before the barrier orders the writes
     // before this work-group's own loads.  (Prefill rows come from rows_kernel.)
@@ -978,7 +1001,7 @@ __device__ __forceinline__ void process_segment_block(const StepArgs &a, int b, 
   for (int pc = 0; pc < npieces; ++pc) {
     const int px = piece_x(pc), py = piece_x(pc + 1);
     const int nch = py - px;
-    const int kstart = r.kbase + px * CHUNK;
+    const int kstart = __builtin_amdgcn_readfirstlane(r.kbase + px * CHUNK);   // uniform
     if (pc > 0) {
       __syncthreads();   // every wave is done with the previous rows
       TableIn tn;
