@@ -687,10 +687,13 @@ __device__ __forceinline__ void process_segment(const StepArgs &a, int b, const 
   const f32x4 wv[4] = {w4[0], w4[1], w4[2], w4[3]};
   const RowIn rin = load_row_in(a, b);
   __builtin_amdgcn_sched_barrier(0);
+  // the token's RoPE (cos, sin) pairs (L = 1), computed while the loads fly
+  float2 csv = make_float2(1.0f, 0.0f);
+  if (a.sliding && tid < 32) csv = rope_cs(pos[0], tid);
 
   __syncthreads();   // the previous segment is done with sh.cs, sh.lrows and the merge buffers
   if (a.sliding) {
-    if (tid < a.L * 32) sh.cs[tid >> 5][tid & 31] = rope_cs(a.positions[b * a.L + (tid >> 5)], tid & 31);
+    if (tid < 32) sh.cs[0][tid] = csv;
     __syncthreads();
   }
   store_table(a, tin, sh.lrows);
@@ -885,6 +888,8 @@ __device__ __forceinline__ void process_segment_block(const StepArgs &a, int b, 
   // new rows' inputs.
   const int shift = a.page_size == 1 ? 0 : 6;
   const int nsteps0 = (piece_x(1) - x + 1) >> 1;
+  const int cs_tk = tid >> 5;   // sliding: this thread's RoPE pair is (token cs_tk, pair tid % 32)
+  const int cs_p = a.sliding ? a.positions[b * a.L + j0 + (cs_tk < nt ? cs_tk : nt - 1)] : 0;
   TableIn tin;
   load_table_in(a, b, r, r.kbase + x * CHUNK, piece_x(1) - x, tin);
   int eu[NR], eunit[NR];
@@ -942,10 +947,14 @@ __device__ __forceinline__ void process_segment_block(const StepArgs &a, int b, 
     }
   }
 
+  // RoPE (cos, sin) of the unit's tokens (512 threads: up to 16 tokens x 32
+  // pairs), computed while the loads fly
+  float2 csv = make_float2(1.0f, 0.0f);
+  if (a.sliding && cs_tk < nt) csv = rope_cs(cs_p, tid & 31);
+
   __syncthreads();   // the previous segment is done with sh.cs, sh.lrows and the stage buffers
   if (a.sliding) {
-    const int tk = tid >> 5;   // 512 threads: up to 16 tokens x 32 pairs
-    if (tk < nt) sh.cs[tk][tid & 31] = rope_cs(a.positions[b * a.L + j0 + tk], tid & 31);
+    if (cs_tk < nt) sh.cs[cs_tk][tid & 31] = csv;
     __syncthreads();
   }
   store_table(a, tin, sh.lrows);
