@@ -298,18 +298,23 @@ __device__ __forceinline__ StageMap stage_map(int t) {
   return m;
 }
 
-__device__ __forceinline__ void stage_load_row(const StepArgs &a, uint32_t row, StageIn &in) {
+// The thread's staged bytes start at this offset into cache row 0 (K or V).
+__device__ __forceinline__ const uint8_t *stage_base(const StepArgs &a) {
   const StageMap m = stage_map(threadIdx.x);
-  const uint8_t *src = (m.v ? a.v_cache : a.k_cache) + (uint64_t)row * ROW + m.part * 32;
+  return (m.v ? a.v_cache : a.k_cache) + m.part * 32;
+}
+
+__device__ __forceinline__ void stage_load_row(const uint8_t *base, uint32_t row, StageIn &in) {
+  const uint8_t *src = base + (uint64_t)row * ROW;
   in.x[0] = *reinterpret_cast<const uint4 *>(src);
   in.x[1] = *reinterpret_cast<const uint4 *>(src + 16);
 }
 
-__device__ __forceinline__ void stage_load(const StepArgs &a, const uint32_t *lrows, int key0,
+// key0 + 63 < MAX_SPLIT_LDS: a piece holds at most MAX_SPLIT_LDS keys and the
+// steps are clamped to the piece's last one.
+__device__ __forceinline__ void stage_load(const uint8_t *base, const uint32_t *lrows, int key0,
                                            StageIn &in) {
-  int kk = key0 + stage_map(threadIdx.x).key;
-  kk = kk < MAX_SPLIT_LDS - 1 ? kk : MAX_SPLIT_LDS - 1;
-  stage_load_row(a, lrows[kk], in);
+  stage_load_row(base, (lrows + stage_map(threadIdx.x).key)[key0], in);
 }
 
 // Slot of chunk q of a V part: odd parts rotate by one.
@@ -936,6 +941,7 @@ __device__ __forceinline__ void process_segment_block(const StepArgs &a, int b, 
   // entries, so they overlap the set-up below -- unless the segment holds new
   // rows, which must be written first.
   const bool early = owned == 0;
+  const uint8_t *sbase = stage_base(a);
   StageIn in[NR];
   if (early) {
     const uint32_t units = (uint32_t)(a.num_rows >> shift);
@@ -943,7 +949,7 @@ __device__ __forceinline__ void process_segment_block(const StepArgs &a, int b, 
     for (int k = 0; k < NR; ++k) {
       uint32_t un = (uint32_t)eunit[k];
       un = un < units ? un : units - 1;
-      stage_load_row(a, (un << shift) + (uint32_t)(eu[k] & (a.page_size - 1)), in[k]);
+      stage_load_row(sbase, (un << shift) + (uint32_t)(eu[k] & (a.page_size - 1)), in[k]);
     }
   }
 
@@ -1040,10 +1046,10 @@ __device__ __forceinline__ void process_segment_block(const StepArgs &a, int b, 
     };
     if (pc > 0 || !early) {   // uniform
 #pragma unroll
-      for (int k = 0; k < NR; ++k) stage_load(a, sh.lrows, step_key(k), in[k]);
+      for (int k = 0; k < NR; ++k) stage_load(sbase, sh.lrows, step_key(k), in[k]);
     }
     stage_store(in[0], sh.stg[0]);
-    stage_load(a, sh.lrows, step_key(NR), in[0]);
+    stage_load(sbase, sh.lrows, step_key(NR), in[0]);
     __syncthreads();
     int s = 0;
     for (; s + NR < nsteps; s += NR) {
@@ -1051,7 +1057,7 @@ __device__ __forceinline__ void process_segment_block(const StepArgs &a, int b, 
       for (int k = 0; k < NR; ++k) {
         compute(s + k);
         stage_store(in[(k + 1) % NR], sh.stg[(s + k + 1) & 1]);
-        stage_load(a, sh.lrows, step_key(s + k + 1 + NR), in[(k + 1) % NR]);
+        stage_load(sbase, sh.lrows, step_key(s + k + 1 + NR), in[(k + 1) % NR]);
         __syncthreads();
       }
     }
