@@ -36,6 +36,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 MFMA_F16_PEAK_TFLOPS = 2500.0
+OPROJ_GEMM_MIN_T = 160   # from this many tokens on the library runs the projection through hipBLASLt
 OPROJ_HIDDEN = 8192   # the decoder layer's model width (the page's [T, 8192] activations)
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "attn_kernel_decode_b32_full_ctx60k-100k_pmc.txt")
 ATTN_SOURCE = os.path.join(ROOT, "paged_fp8_kv_amd", "csrc", "attn_splitk.hip")
@@ -293,14 +294,23 @@ def main():
         o_ms = [hip_elapsed_ms(s0, e0) for s0, e0 in oevs]
         o_avg = sum(o_ms) / len(o_ms)
         obytes = OPROJ_HIDDEN * 1024 * 2 + w.T * 1024 * 2 + w.T * OPROJ_HIDDEN * 2
-        oproj = {"kernel": "oproj_kernel (y = out . o^T, bf16 MFMA, fp32 sums)",
-                 "hidden": OPROJ_HIDDEN, "bound": "hbm", "algorithmic_bytes_per_launch": obytes,
-                 "avg_launch_us": round(o_avg * 1e3, 2),
-                 "achieved": round(obytes / (o_avg * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBS,
-                 "unit": "GB/s", "frac": round(obytes / (o_avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        oflops = 2 * w.T * 1024 * OPROJ_HIDDEN
+        # the roofline that bounds it: bytes at the HBM peak or products at the
+        # bf16 MFMA peak (the same 2.5 PFLOP/s as fp16), whichever takes longer
+        mfma_bound = oflops / (MFMA_F16_PEAK_TFLOPS * 1e12) > obytes / (HBM_PEAK_GBS * 1e9)
+        if mfma_bound:
+            ach, peak, unit = oflops / (o_avg * 1e-3) / 1e12, MFMA_F16_PEAK_TFLOPS, "TFLOP/s"
+        else:
+            ach, peak, unit = obytes / (o_avg * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s"
+        oproj = {"kernel": ("hipBLASLt bf16 GEMM (y = out . o^T, fp32 sums)" if w.T >= OPROJ_GEMM_MIN_T
+                            else "oproj_kernel (y = out . o^T, bf16 MFMA, fp32 sums)"),
+                 "hidden": OPROJ_HIDDEN, "tokens": w.T, "bound": "mfma" if mfma_bound else "hbm",
+                 "algorithmic_bytes_per_launch": obytes, "algorithmic_flops_per_launch": oflops,
+                 "avg_launch_us": round(o_avg * 1e3, 2), "achieved": round(ach, 1), "peak": peak,
+                 "unit": unit, "frac": round(ach / peak, 4),
                  "avg_launch_us_from": f"HIP events around each of {args.steps} eager launches"}
-        log(f"o-projection kernel avg {o_avg * 1e3:.2f} us ({oproj['achieved']} GB/s on "
-            f"{obytes / 1e6:.1f} MB)")
+        log(f"o-projection avg {o_avg * 1e3:.2f} us ({oproj['achieved']} {unit}, "
+            f"{obytes / 1e6:.1f} MB, {oflops / 1e9:.1f} GFLOP)")
 
     cold = None
     if args.cold_reps > 0:

@@ -177,7 +177,12 @@ int museattn_attn_step_profiled(const void *qkv, const int32_t *positions, const
  *   hidden    output features, a multiple of 64 in [64, MUSEATTN_MAX_HIDDEN]
  *   y         bf16 [T][hidden], 8-byte aligned, overlapping neither a nor o_weight
  *   stream    hipStream_t the work is enqueued on
- * Device pointers, owned by the caller; nothing is allocated.  Statuses:
+ * Device pointers, owned by the caller.  Up to 159 tokens the library's own
+ * kernel runs; from 160 tokens on the product is a plain GEMM run by
+ * hipBLASLt without a workspace.  Its handle (one per device) and its plan (one
+ * per (T, hidden), at most 64 kept) are made at a shape's first call: a caller
+ * that captures the call in a graph runs the shape once before capturing it.
+ * If hipBLASLt cannot run a shape, the library's own kernel does.  Statuses:
  * MUSEATTN_ERR_NULL, _PARAM (T or hidden), _ALIGN, _ALIAS, _LAUNCH. */
 int museattn_oproj(const void *a, const void *o_weight, int T, int hidden, void *y, void *stream);
 

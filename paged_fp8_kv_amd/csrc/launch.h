@@ -9,4 +9,7 @@ void launch_combine(const StepArgs &a, hipStream_t stream);
 void launch_rows(const StepArgs &a, hipStream_t stream);
 void launch_oproj(const uint16_t *a, const uint16_t *o, uint16_t *y, int T, int N,
                   hipStream_t stream);
+// hipBLASLt GEMM for the projection; false if nothing was enqueued
+bool gemm_oproj(const uint16_t *a, const uint16_t *o, uint16_t *y, int T, int N,
+                hipStream_t stream);
 }  // namespace museattn

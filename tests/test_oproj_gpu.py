@@ -31,12 +31,13 @@ def _need_gpu():
 
 
 @pytest.mark.parametrize("T,hidden", [(1, 64), (7, 8192), (32, 8192), (33, 1088), (64, 8192),
-                                      (65, 64), (100, 2048), (129, 1088), (256, 8192),
-                                      (753, 8192)])
+                                      (65, 64), (100, 2048), (129, 1088), (159, 1088),
+                                      (160, 8192), (256, 8192), (753, 8192), (1024, 64)])
 def test_oproj_alone(T, hidden):
-    """T <= 64 runs the register kernel, larger T the LDS-tiled one (128 x 128
-    tiles: hidden 64 and 1088 leave a partial row tile, T 65, 129 and 753 a
-    partial token tile)."""
+    """Up to 159 tokens the library's kernel runs (32 rows of o per work-group,
+    64-token passes: T 33, 65, 100, 129 and 159 end inside a pass); from 160 on
+    the hipBLASLt GEMM (T 159 and 160 sit on either side of the switch, hidden
+    64 is its smallest shape)."""
     a = W.oproj_input(70 + T, T)
     o = W.oproj_weight(71, hidden)
     y = torch.empty(T, hidden, dtype=torch.bfloat16, device="cuda")
