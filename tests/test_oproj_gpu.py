@@ -86,3 +86,34 @@ def test_step_then_oproj(case):
     want = O.oproj(out, o.double().cpu().numpy())
     compare_out(d["out"].float().cpu().numpy().reshape(w.T, 1024), out, f"{name} out")
     compare_out(y.float().cpu().numpy(), want, f"{name} y")
+
+
+@pytest.mark.parametrize("T", [32, 753])
+def test_oproj_graph_replays_match_eager(T):
+    """The projection captured into a HIP graph -- the library's kernel at 32
+    tokens, the hipBLASLt GEMM at 753 -- gives the eager call's bytes on every
+    replay, with eager calls in between."""
+    a = W.oproj_input(90 + T, T).cuda()
+    o = W.oproj_weight(91, 8192).cuda()
+    y = torch.empty(T, 8192, dtype=torch.bfloat16, device="cuda")
+    P.oproj(a, o, y)   # first call of the shape: makes the plan outside the capture
+    torch.cuda.synchronize()
+    eager = y.clone()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        P.oproj(a, o, y)   # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        P.oproj(a, o, y)
+    for i in range(3):
+        y.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, eager), f"replay {i} differs from the eager call"
+        P.oproj(a, o, y)   # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(y, eager)
