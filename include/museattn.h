@@ -3,20 +3,29 @@
  * paged FP8 E4M3 KV cache, for AMD Instinct MI355X (gfx950).
  *
  * The operation is the one defined on the task page "Gated attention decode
- * (muse_attention_decode)", section "What to compute": for every request b
- * and block token j (position p = positions[b*L + j]) of one decode step
- * (L = 1), one causal verify block (L <= 8) or one causal prefill block (up to
- * 16384 tokens; the attention part of the prefill task page "Prefill layer",
- * section "Shapes", over the same cache):
- *
- *   q, k, v, gate = split(qkv row)              (section "What to compute")
- *   q = rmsnorm(q) * w_q * q_scale ; k = rmsnorm(k) * w_k
- *   q, k = rope(q, p), rope(k, p)               sliding-window layers only
- *   cache row(b, p) <- fp8(k / kv_scale), fp8(v / kv_scale)
- *   a = softmax(q . K^T / 8) . V                keys 0..p (full layer) or
- *                                               p-2047..p (sliding layer,
- *                                               section "Shapes")
- *   out = rmsnorm(a) * w_o * sigmoid(gate)      per head, bf16
+ * (muse_attention_decode)", section "What to compute" (the window and the
+ * causal rule come from its section "Shapes"; blocks of more than 8 tokens
+ * are the attention part of the prefill task page "Prefill layer", section
+ * "Shapes", over the same cache).  One call serves B requests of L block
+ * tokens each: a decode step (L = 1), a causal verify block (L <= 8) or a
+ * causal prefill block (up to 16384 tokens).  For block token j of request b,
+ * at position p = positions[b*L + j]:
+ *   1. its bf16 row of the fused projection is cut into 16 query heads, 2 key
+ *      heads, 2 value heads and 16 gate heads of 64 values each;
+ *   2. every query and key head is RMS-normalised over its 64 values and
+ *      multiplied by a per-dimension weight; the queries are then scaled by
+ *      q_scale;
+ *   3. on sliding-window layers the query and key heads are rotated by the
+ *      angle set of position p (half-split rotary embedding);
+ *   4. its key and value heads, divided by kv_scale and rounded to E4M3, are
+ *      stored in the token's cache row;
+ *   5. query head h attends to KV head h / 8 with scores scaled by 1/8, over
+ *      the cached keys at positions 0..p on a full layer or p-2047..p on a
+ *      sliding one (the block's own new rows included, read back from the
+ *      cache);
+ *   6. each head's attention result is RMS-normalised, multiplied by its
+ *      weight and by the logistic sigmoid of the head's gate, and stored as
+ *      bf16.
  *
  * Shapes per GPU shard (section "Shapes"): 16 query heads, 2 KV heads, head
  * dim 64; query head h reads KV head h / 8.  The fused row is bf16
@@ -37,10 +46,12 @@
  *  - the library never allocates, frees, synchronises or reads device values
  *    on the host; all work is enqueued on `stream`, so a call can be captured
  *    into a HIP graph.  Nothing is cached between calls.
- *  - k_cache / v_cache are written only at the B*L new rows.  qkv, out,
- *    k_cache, v_cache (num_rows rows each) and workspace must not overlap
- *    one another; `workspace` holds scratch data of one call (it must not be
- *    shared by calls that may run concurrently).
+ *  - k_cache / v_cache are written only at the B*L new rows.  The buffers
+ *    the step writes (out, k_cache and v_cache of num_rows rows each, the
+ *    workspace) must not overlap one another or any buffer it reads (qkv,
+ *    positions, table, seq_lens, the norm weights); `workspace` holds scratch
+ *    data of one call (it must not be shared by calls that may run
+ *    concurrently).
  *  - device-side indices are clamped into the extents the host validated
  *    (rows into [0, num_rows), positions into [0, max_seq_len)), so
  *    inconsistent device data gives wrong numbers, never an out-of-bounds
@@ -80,8 +91,12 @@ enum museattn_status {
   MUSEATTN_ERR_PAGE_SIZE = -2,    /* page_size is not 1 or 64 */
   MUSEATTN_ERR_LAYER_KIND = -3,   /* layer_kind is not FULL or SLIDING */
   MUSEATTN_ERR_SHAPE = -4,        /* B (1..1024), L (1..16384), B * ceil(L / 16)
-                                     (L > 8) above 4096, max_seq_len or
-                                     num_rows out of range */
+                                     (L > 8) above 4096, max_seq_len, num_rows
+                                     (a multiple of page_size below 2^32) out
+                                     of range, or a plan whose chunk count
+                                     could reach 2^31 (B * ceil(max_seq_len /
+                                     32) roughly, per 16-token group beyond
+                                     L = 8) */
   MUSEATTN_ERR_TABLE = -5,        /* table_stride < ceil(max_seq_len / page_size) */
   MUSEATTN_ERR_ALIGN = -6,        /* k_cache, v_cache, qkv or a norm weight not
                                      16-byte aligned, out not 8-byte aligned,
@@ -90,7 +105,10 @@ enum museattn_status {
                                      or not 256-byte aligned */
   MUSEATTN_ERR_PARAM = -8,        /* kv_scale, eps, q_scale, rope_base or
                                      work_groups out of range */
-  MUSEATTN_ERR_ALIAS = -9,        /* two of qkv, out, k_cache, v_cache, workspace overlap */
+  MUSEATTN_ERR_ALIAS = -9,        /* a buffer the step writes (out, k_cache,
+                                     v_cache, workspace) overlaps another one
+                                     of them or one it reads (qkv, positions,
+                                     table, seq_lens, a norm weight) */
   MUSEATTN_ERR_LAUNCH = -10       /* a kernel launch failed */
 };
 

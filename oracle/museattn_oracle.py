@@ -5,22 +5,26 @@ cpu_baseline leg may import this module.  The product path (the HIP library and
 its Python binding in paged_fp8_kv_amd/) never imports, links or calls it, and
 this module imports nothing from the product path.
 
-What it computes is the "What to compute" listing of the task page "Gated
-attention decode (muse_attention_decode)", restated as a plain, slow, float64
-program (numpy matmul and exp are the only library steps):
-
-  per request b and block token j, at position p = positions[b*L + j]
-    q, k, v, gate = split(qkv row)             fused projection row
-    q <- rmsnorm(q) * 5.473 ; k <- rmsnorm(k)  QK-norm
-    q, k <- rope(q, p), rope(k, p)             sliding-window layers only
-    cache row(b, p) <- fp8(k), fp8(v)          written before any attention
-    a = softmax(q . K^T / 8) . V               keys 0..p (full) or the last
-                                               2048 positions p-2047..p (sliding)
-    out = rmsnorm(a) * sigmoid(gate)           per head, bf16 [B, L, 16*64]
-
-and the output projection that follows it in the decoder layer (task page
-"Whole decoder layer", section "What to compute"; the all-reduce after it is
-the identity on one GPU):  y = out @ o^T, o [hidden, 1024].
+What it computes is the operation of the task page "Gated attention decode
+(muse_attention_decode)", section "What to compute", written out as a plain,
+slow, float64 program (numpy matmul and exp are the only library steps).  For
+each request b and block token j, at position p = positions[b*L + j]:
+  1. the fused projection row is cut into query, key, value and gate heads;
+  2. query and key heads are RMS-normalised with their weights, and the
+     queries are multiplied by the q scale (5.473 on the page);
+  3. on sliding-window layers both are rotated by position p;
+  4. all the block's new key and value heads are rounded to fp8 and stored in
+     their cache rows before any attention reads the cache;
+  5. each query head takes a softmax of its scores (dot products with the
+     cached keys of its KV head, divided by 8) over positions 0..p on a full
+     layer or the last 2048 positions p-2047..p on a sliding one, and sums
+     the matching cached values with those weights;
+  6. each head's result is RMS-normalised with its weight, multiplied by the
+     sigmoid of its gate, and returned as out [B, L, 16*64].
+It also holds the output projection that follows the step in the decoder
+layer (task page "Whole decoder layer", section "What to compute"; the
+all-reduce after it is the identity on one GPU): y = out @ o^T, o [hidden,
+1024].
 
 Readings where the page is silent:
   * qkv row layout [q 16x64 | k 2x64 | v 2x64 | gate 16x64], head-major.

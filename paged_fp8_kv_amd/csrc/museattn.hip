@@ -49,13 +49,62 @@ Layout layout(int B, int L, int work_groups) {
   return ly;
 }
 
+// A segment start-up (batch of loads + first rows) is worth about this many
+// 32-key chunks of one work-group's streaming (measured on MI355X).
+#ifndef MUSEATTN_SEG_COST_VERIFY
+#define MUSEATTN_SEG_COST_VERIFY 16
+#endif
+#ifndef MUSEATTN_SEG_COST_PREFILL
+#define MUSEATTN_SEG_COST_PREFILL 16
+#endif
+#ifndef MUSEATTN_SEG_COST_DECODE
+#define MUSEATTN_SEG_COST_DECODE 14
+#endif
+// The work-group holding a unit's last chunk also writes its new rows
+// (prefill rows are written by their own kernel).
+#ifndef MUSEATTN_END_COST_DECODE
+#define MUSEATTN_END_COST_DECODE 0
+#endif
+#ifndef MUSEATTN_END_COST_VERIFY
+#define MUSEATTN_END_COST_VERIFY 8
+#endif
+constexpr int MAX_COST = 64;
+static_assert(MUSEATTN_SEG_COST_VERIFY <= MAX_COST && MUSEATTN_SEG_COST_PREFILL <= MAX_COST &&
+                  MUSEATTN_SEG_COST_DECODE <= MAX_COST && MUSEATTN_END_COST_DECODE <= MAX_COST &&
+                  MUSEATTN_END_COST_VERIFY <= MAX_COST,
+              "plan costs are bounded for the 32-bit prefix sums");
+
+int seg_cost(int L) {
+  return L == 1 ? MUSEATTN_SEG_COST_DECODE
+                : (L <= 8 ? MUSEATTN_SEG_COST_VERIFY : MUSEATTN_SEG_COST_PREFILL);
+}
+int end_cost(int L) {
+  return L == 1 ? MUSEATTN_END_COST_DECODE : (L <= 8 ? MUSEATTN_END_COST_VERIFY : 0);
+}
+
+// Chunk-equivalents of the plan's cost space that one unit can occupy at
+// most: its key range in 32-key chunks (one more for the alignment of a
+// sliding window's start) plus the start-up and end costs.
+int64_t max_unit_cost(int L, int max_seq_len, int layer_kind) {
+  int64_t keys = max_seq_len;
+  if (layer_kind == MUSEATTN_SLIDING) {
+    const int64_t win = (int64_t)WINDOW + unit_tokens(L) - 1;
+    keys = keys < win ? keys : win;
+  }
+  return (keys + CHUNK - 1) / CHUNK + 1 + 2 * MAX_COST;
+}
+
 int check_shapes(int B, int L, int max_seq_len, int page_size, int layer_kind,
                  const museattn_params *params) {
   if (page_size != 1 && page_size != 64) return MUSEATTN_ERR_PAGE_SIZE;
   if (layer_kind != MUSEATTN_FULL && layer_kind != MUSEATTN_SLIDING) return MUSEATTN_ERR_LAYER_KIND;
   if (B < 1 || B > MAX_BATCH || L < 1 || L > MAX_L || max_seq_len < L || max_seq_len > MAX_SEQ)
     return MUSEATTN_ERR_SHAPE;
-  if ((int64_t)B * units_per_request(L) > MAX_UNITS) return MUSEATTN_ERR_SHAPE;
+  const int64_t units = (int64_t)B * units_per_request(L);
+  if (units > MAX_UNITS) return MUSEATTN_ERR_SHAPE;
+  // the kernels keep the plan's chunk prefix sums in 32-bit integers
+  if (units * max_unit_cost(L, max_seq_len, layer_kind) >= (int64_t(1) << 31))
+    return MUSEATTN_ERR_SHAPE;
   if (params == nullptr) return MUSEATTN_ERR_NULL;
   if (params->work_groups < 0 || params->work_groups > MAX_WORK_GROUPS) return MUSEATTN_ERR_PARAM;
   return MUSEATTN_OK;
@@ -77,12 +126,14 @@ const char *museattn_strerror(int status) {
     case MUSEATTN_ERR_PAGE_SIZE: return "page_size must be 1 or 64";
     case MUSEATTN_ERR_LAYER_KIND: return "layer_kind must be MUSEATTN_FULL or MUSEATTN_SLIDING";
     case MUSEATTN_ERR_SHAPE:
-      return "B, L, B * ceil(L / 16) (L > 8), max_seq_len or num_rows out of range";
+      return "B, L, B * ceil(L / 16) (L > 8), max_seq_len, the plan's chunk count or num_rows "
+             "out of range";
     case MUSEATTN_ERR_TABLE: return "table_stride < ceil(max_seq_len / page_size)";
     case MUSEATTN_ERR_ALIGN: return "misaligned pointer (caches, qkv and weights need 16 bytes, out 8)";
     case MUSEATTN_ERR_WORKSPACE: return "workspace too small or not 256-byte aligned";
     case MUSEATTN_ERR_PARAM: return "kv_scale, eps, q_scale, rope_base or work_groups out of range";
-    case MUSEATTN_ERR_ALIAS: return "buffers overlap (qkv, out, k_cache, v_cache, workspace)";
+    case MUSEATTN_ERR_ALIAS:
+      return "a written buffer (out, k_cache, v_cache, workspace) overlaps another buffer";
     case MUSEATTN_ERR_LAUNCH: return "kernel launch failed";
     default: return "unknown status";
   }
@@ -111,7 +162,8 @@ int museattn_check_args(const void *qkv, const int32_t *positions, const int32_t
   if (!params->q_norm_w || !params->k_norm_w || !params->o_norm_w) return MUSEATTN_ERR_NULL;
   const int st = check_shapes(B, L, max_seq_len, page_size, layer_kind, params);
   if (st != MUSEATTN_OK) return st;
-  if (num_rows < page_size || num_rows % page_size != 0 || num_rows > (int64_t(1) << 32))
+  // rows are addressed as 32-bit indices on the device
+  if (num_rows < page_size || num_rows % page_size != 0 || num_rows >= (int64_t(1) << 32))
     return MUSEATTN_ERR_SHAPE;
   if ((int64_t)table_stride * page_size < max_seq_len || table_stride < 1) return MUSEATTN_ERR_TABLE;
   // the kernels read q, k, v and gate slices of 16 B, the norm weights as
@@ -129,7 +181,8 @@ int museattn_check_args(const void *qkv, const int32_t *positions, const int32_t
       workspace_bytes < museattn_workspace_bytes(B, L, max_seq_len, page_size, layer_kind, params))
     return MUSEATTN_ERR_WORKSPACE;
   // the buffers the step writes (out, the caches' new rows, the workspace)
-  // must not overlap what it reads or each other
+  // must not overlap each other or anything the step reads: every work-group
+  // re-reads seq_lens, positions and the table while others write
   struct Span {
     uintptr_t lo, hi;
   };
@@ -138,12 +191,19 @@ int museattn_check_args(const void *qkv, const int32_t *positions, const int32_t
   };
   auto meet = [](Span x, Span y) { return x.lo < y.hi && y.lo < x.hi; };
   const uint64_t T = (uint64_t)B * L;
-  const Span sq = span(qkv, T * QKV_W * 2), so = span(out, T * HQ * D * 2);
-  const Span sk = span(k_cache, (uint64_t)num_rows * ROW), sv = span(v_cache, (uint64_t)num_rows * ROW);
-  const Span sw = span(workspace, workspace_bytes);
-  if (meet(so, sq) || meet(so, sk) || meet(so, sv) || meet(so, sw) || meet(sw, sq) ||
-      meet(sw, sk) || meet(sw, sv) || meet(sk, sv) || meet(sk, sq) || meet(sv, sq))
-    return MUSEATTN_ERR_ALIAS;
+  const Span written[4] = {span(out, T * HQ * D * 2), span(k_cache, (uint64_t)num_rows * ROW),
+                           span(v_cache, (uint64_t)num_rows * ROW),
+                           span(workspace, workspace_bytes)};
+  const Span read[7] = {span(qkv, T * QKV_W * 2), span(positions, T * 4),
+                        span(table, (uint64_t)B * table_stride * 4), span(seq_lens, (uint64_t)B * 4),
+                        span(params->q_norm_w, D * 4), span(params->k_norm_w, D * 4),
+                        span(params->o_norm_w, D * 4)};
+  for (int i = 0; i < 4; ++i) {
+    for (int k = i + 1; k < 4; ++k)
+      if (meet(written[i], written[k])) return MUSEATTN_ERR_ALIAS;
+    for (const Span &r : read)
+      if (meet(written[i], r)) return MUSEATTN_ERR_ALIAS;
+  }
   return MUSEATTN_OK;
 }
 
@@ -190,28 +250,8 @@ int museattn_attn_step_profiled(const void *qkv, const int32_t *positions, const
   a.page_size = page_size;
   a.sliding = layer_kind == MUSEATTN_SLIDING;
   a.work_groups = ly.work_groups;
-  // a segment start-up (batch of loads + first rows) is worth about this many
-  // 32-key chunks of one work-group's streaming (measured on MI355X)
-#ifndef MUSEATTN_SEG_COST_VERIFY
-#define MUSEATTN_SEG_COST_VERIFY 16
-#endif
-#ifndef MUSEATTN_SEG_COST_PREFILL
-#define MUSEATTN_SEG_COST_PREFILL 16
-#endif
-#ifndef MUSEATTN_SEG_COST_DECODE
-#define MUSEATTN_SEG_COST_DECODE 14
-#endif
-  a.seg_cost = L == 1 ? MUSEATTN_SEG_COST_DECODE
-                      : (L <= 8 ? MUSEATTN_SEG_COST_VERIFY : MUSEATTN_SEG_COST_PREFILL);
-#ifndef MUSEATTN_END_COST_DECODE
-#define MUSEATTN_END_COST_DECODE 0
-#endif
-#ifndef MUSEATTN_END_COST_VERIFY
-#define MUSEATTN_END_COST_VERIFY 8
-#endif
-  // the work-group holding a unit's last chunk also writes its new rows
-  // (prefill rows are written by their own kernel)
-  a.end_cost = L == 1 ? MUSEATTN_END_COST_DECODE : (L <= 8 ? MUSEATTN_END_COST_VERIFY : 0);
+  a.seg_cost = seg_cost(L);
+  a.end_cost = end_cost(L);
   a.tb = unit_tokens(L);
   a.nblk = units_per_request(L);
   a.nunits = B * a.nblk;

@@ -35,8 +35,8 @@ def test_strerror_covers_all_statuses():
 
 
 # fake device addresses: far apart, 256-byte aligned
-BASE = 1 << 40
-A = {k: BASE + i * (1 << 34) for i, k in enumerate(
+BASE = 1 << 44
+A = {k: BASE + i * (1 << 43) for i, k in enumerate(
     ["qkv", "pos", "table", "seq", "kc", "vc", "out", "ws", "wq", "wk", "wo"])}
 
 
@@ -63,6 +63,12 @@ def _check(**kw):
 
 def test_valid_arguments_pass():
     assert _check() == 0
+    assert _check(num_rows=(1 << 32) - 1) == 0
+    assert _check(page_size=64, num_rows=(1 << 32) - 64, table_stride=16) == 0
+    assert _check(B=32, max_seq_len=1 << 30, table_stride=1 << 30) == 0
+    assert _check(B=1024, max_seq_len=1 << 30, table_stride=1 << 30, layer_kind=P.SLIDING) == 0
+    assert _check(B=1024, max_seq_len=1 << 20, table_stride=1 << 20) == 0
+    assert _check(wq=A["wk"]) == 0            # read-only inputs may share memory
     assert _check(page_size=64, table_stride=16, num_rows=64 * 100) == 0
     assert _check(L=8, layer_kind=P.SLIDING) == 0
     assert _check(work_groups=65535) == 0
@@ -105,6 +111,15 @@ def test_valid_arguments_pass():
     (dict(ws=A["vc"] + 1024), -9),           # workspace inside the V cache
     (dict(ws=A["out"]), -9),                 # workspace over out
     (dict(kc=A["vc"]), -9),                  # one array for both caches
+    (dict(num_rows=1 << 32), -4),            # rows are 32-bit indices on the device
+    (dict(page_size=64, num_rows=(1 << 32), table_stride=16), -4),
+    # plans whose 32-bit chunk prefix sums could overflow
+    (dict(B=64, max_seq_len=1 << 30, table_stride=1 << 30), -4),
+    (dict(B=1024, max_seq_len=1 << 26, table_stride=1 << 26), -4),
+    (dict(ws=A["pos"]), -9),                 # workspace over the positions
+    (dict(out=A["table"] + 64), -9),         # out over the table
+    (dict(kc=A["seq"] - 4096), -9),          # K cache over seq_lens
+    (dict(ws=A["wk"] - 256), -9),            # workspace over a norm weight
 ])
 def test_invalid_arguments_are_rejected(kw, status):
     assert _check(**kw) == status

@@ -74,7 +74,7 @@ EDGE = [
     ("empty-context", 2, 1, 0, W.FULL, 1, 1.0),
     ("ctx10-sliding", 1, 1, 10, W.SLIDING, 64, 1.0),
     ("ctx2047-sliding-b3", 3, 1, 2047, W.SLIDING, 64, 1.0),
-    ("b5-L8-sliding-spread", 5, 8, (4000, 6000), W.SLIDING, 1, 1.0),
+    ("b5-L8-sliding-ctx6000-spread", 5, 8, (3000, 6000), W.SLIDING, 1, 1.0),
     ("b4-full-ctx3000-p64", 4, 1, 3000, W.FULL, 64, 1.0),
     ("b4-L8-sliding-window-edges", 4, 8, (2038, 2058), W.SLIDING, 1, 1.0),
     ("b4-L8-full-ctx6000", 4, 8, 6000, W.FULL, 64, 1.0),
