@@ -184,6 +184,33 @@ int museattn_attn_step_profiled(const void *qkv, const int32_t *positions, const
                                 size_t workspace_bytes, void *attn_start_event,
                                 void *attn_end_event);
 
+/* Bytes of the library's static device scratch (museattn_attn_step_noalloc). */
+#define MUSEATTN_STATIC_SCRATCH_BYTES (32u << 20)
+
+/* museattn_attn_step for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation.  Same arguments as museattn_attn_step without the workspace:
+ * the step's scratch (plan and split-K partials) lives in a fixed device array
+ * of MUSEATTN_STATIC_SCRATCH_BYTES inside the library, one per GPU, held until
+ * the process ends.  The call allocates and frees nothing; its first call on a
+ * device looks up that array's address there (hipGetSymbolAddress, with the
+ * stream's device current) and keeps it.
+ *   - Shapes whose museattn_workspace_bytes(...) exceeds the array are
+ *     rejected with MUSEATTN_ERR_WORKSPACE (32 MiB holds every decode shape,
+ *     verify blocks of L = 8 up to B = 736, prefill blocks up to about 240
+ *     16-token groups).
+ *   - Every call on one GPU shares the array: calls that may overlap in time
+ *     on one GPU (other streams, concurrent graph replays) race and must be
+ *     serialised by the caller.  Each call rewrites all it reads of the array,
+ *     so nothing needs clearing between calls.
+ * Statuses: those of museattn_attn_step (MUSEATTN_ERR_LAUNCH also if the
+ * array's address cannot be looked up). */
+int museattn_attn_step_noalloc(const void *qkv, const int32_t *positions, const int32_t *table,
+                               const int32_t *seq_lens, void *k_cache, void *v_cache,
+                               float kv_scale, int page_size, int layer_kind, void *out,
+                               void *stream, int B, int L, int table_stride, int max_seq_len,
+                               int64_t num_rows, const museattn_params *params);
+
 /* The attention output projection of the decoder layer (task page "Whole
  * decoder layer", section "What to compute": the gated attention output times
  * o^T; on one GPU the all-reduce that follows is the identity):

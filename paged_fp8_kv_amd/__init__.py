@@ -32,7 +32,9 @@ STATUS = {
 # every symbol include/museattn.h declares
 EXPORTS = ("museattn_abi_version", "museattn_strerror", "museattn_workspace_bytes",
            "museattn_check_args", "museattn_attn_step", "museattn_attn_step_profiled",
-           "museattn_work_groups", "museattn_oproj", "museattn_attn_step_oproj")
+           "museattn_work_groups", "museattn_oproj", "museattn_attn_step_oproj",
+           "museattn_attn_step_noalloc")
+STATIC_SCRATCH_BYTES = 32 << 20   # MUSEATTN_STATIC_SCRATCH_BYTES
 
 
 class Params(ctypes.Structure):
@@ -84,6 +86,8 @@ def lib() -> ctypes.CDLL:
         L.museattn_attn_step_profiled.argtypes = L.museattn_attn_step.argtypes + [vp, vp]
         L.museattn_attn_step_oproj.restype = i32
         L.museattn_attn_step_oproj.argtypes = L.museattn_attn_step.argtypes + [vp, i32, vp, vp, vp]
+        L.museattn_attn_step_noalloc.restype = i32
+        L.museattn_attn_step_noalloc.argtypes = common + [vp, i32, i32, i32, i32, i64, pp]
         L.museattn_oproj.restype = i32
         L.museattn_oproj.argtypes = [vp, vp, i32, i32, vp, vp]
         _lib = L
@@ -137,23 +141,11 @@ def _need(cond, msg):
         raise ValueError(msg)
 
 
-def attn_step(qkv, positions, table, seq_lens, k_cache, v_cache, kv_scale, page_size,
-              layer_kind, out, stream=None, *, q_norm_w, k_norm_w, o_norm_w, max_seq_len,
-              workspace=None, eps=DEFAULT_EPS, q_scale=DEFAULT_Q_SCALE,
-              rope_base=DEFAULT_ROPE_BASE, work_groups=0, attn_events=None, o_weight=None,
-              y=None, oproj_events=None):
-    """One attention step on torch tensors (see include/museattn.h).
-
-    qkv bf16 [B*L, 2304]; positions int32 [B*L]; table int32 [B, stride];
-    seq_lens int32 [B]; k_cache / v_cache uint8 [num_rows, 2, 64] (or any
-    uint8 view of that many bytes); out bf16 [B, L, 1024]; norm weights
-    float32 [64]; workspace uint8 of >= workspace_bytes(...) bytes or None
-    (then allocated here with torch).  stream: a torch.cuda.Stream, a raw
-    hipStream_t int, or None for the current stream.  attn_events: optional
-    (start, end) torch.cuda.Event pair recorded around the attention kernel
-    (museattn_attn_step_profiled).  o_weight (bf16 [hidden, 1024]) and y
-    (bf16 [B*L, hidden]) given: the output projection follows the step
-    (museattn_attn_step_oproj), oproj_events around its kernel."""
+def _step_args(qkv, positions, table, seq_lens, k_cache, v_cache, kv_scale, page_size,
+               layer_kind, out, stream, q_norm_w, k_norm_w, o_norm_w, max_seq_len, eps,
+               q_scale, rope_base, work_groups):
+    """Checks the step's tensors; returns the C arguments up to `params`,
+    the params struct (kept alive by the caller) and B, L."""
     import torch
 
     B = int(seq_lens.shape[0])
@@ -181,10 +173,6 @@ def attn_step(qkv, positions, table, seq_lens, k_cache, v_cache, kv_scale, page_
     _need(k_cache.numel() == v_cache.numel(), "k_cache and v_cache must hold the same rows")
     num_rows = k_cache.numel() // ROW_BYTES
     params = make_params(q_norm_w, k_norm_w, o_norm_w, eps, q_scale, rope_base, work_groups)
-    need = workspace_bytes(B, L, max_seq_len, page_size, layer_kind, work_groups)
-    if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
-    _need(workspace.is_cuda and workspace.dtype == torch.uint8, "workspace must be a uint8 device tensor")
     if stream is None:
         stream_ptr = torch.cuda.current_stream(dev).cuda_stream
     elif hasattr(stream, "cuda_stream"):
@@ -194,8 +182,39 @@ def attn_step(qkv, positions, table, seq_lens, k_cache, v_cache, kv_scale, page_
     args = (qkv.data_ptr(), positions.data_ptr(), table.data_ptr(), seq_lens.data_ptr(),
             k_cache.data_ptr(), v_cache.data_ptr(), float(kv_scale), int(page_size),
             int(layer_kind), out.data_ptr(), stream_ptr, B, L, int(table.shape[1]),
-            int(max_seq_len), int(num_rows), ctypes.byref(params), workspace.data_ptr(),
-            int(workspace.numel()))
+            int(max_seq_len), int(num_rows), ctypes.byref(params))
+    return args, params, B, L
+
+
+def attn_step(qkv, positions, table, seq_lens, k_cache, v_cache, kv_scale, page_size,
+              layer_kind, out, stream=None, *, q_norm_w, k_norm_w, o_norm_w, max_seq_len,
+              workspace=None, eps=DEFAULT_EPS, q_scale=DEFAULT_Q_SCALE,
+              rope_base=DEFAULT_ROPE_BASE, work_groups=0, attn_events=None, o_weight=None,
+              y=None, oproj_events=None):
+    """One attention step on torch tensors (see include/museattn.h).
+
+    qkv bf16 [B*L, 2304]; positions int32 [B*L]; table int32 [B, stride];
+    seq_lens int32 [B]; k_cache / v_cache uint8 [num_rows, 2, 64] (or any
+    uint8 view of that many bytes); out bf16 [B, L, 1024]; norm weights
+    float32 [64]; workspace uint8 of >= workspace_bytes(...) bytes or None
+    (then allocated here with torch).  stream: a torch.cuda.Stream, a raw
+    hipStream_t int, or None for the current stream.  attn_events: optional
+    (start, end) torch.cuda.Event pair recorded around the attention kernel
+    (museattn_attn_step_profiled).  o_weight (bf16 [hidden, 1024]) and y
+    (bf16 [B*L, hidden]) given: the output projection follows the step
+    (museattn_attn_step_oproj), oproj_events around its kernel."""
+    import torch
+
+    args, params, B, L = _step_args(qkv, positions, table, seq_lens, k_cache, v_cache, kv_scale,
+                                     page_size, layer_kind, out, stream, q_norm_w, k_norm_w,
+                                     o_norm_w, max_seq_len, eps, q_scale, rope_base, work_groups)
+    T = B * L
+    dev = qkv.device
+    need = workspace_bytes(B, L, max_seq_len, page_size, layer_kind, work_groups)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    _need(workspace.is_cuda and workspace.dtype == torch.uint8, "workspace must be a uint8 device tensor")
+    args = args + (workspace.data_ptr(), int(workspace.numel()))
     if o_weight is not None or y is not None:
         _need(o_weight is not None and y is not None, "o_weight and y go together")
         _need(attn_events is None, "attn_events are not recorded with the projection")
@@ -214,6 +233,22 @@ def attn_step(qkv, positions, table, seq_lens, k_cache, v_cache, kv_scale, page_
                                                attn_events[1].cuda_event)
     if st != OK:
         raise MuseAttnError(st, "museattn_attn_step")
+    return out
+
+
+def attn_step_noalloc(qkv, positions, table, seq_lens, k_cache, v_cache, kv_scale, page_size,
+                      layer_kind, out, stream=None, *, q_norm_w, k_norm_w, o_norm_w,
+                      max_seq_len, eps=DEFAULT_EPS, q_scale=DEFAULT_Q_SCALE,
+                      rope_base=DEFAULT_ROPE_BASE, work_groups=0):
+    """museattn_attn_step_noalloc: the step with its scratch in the library's
+    static device array (no allocation by the library or here).  Calls that may
+    overlap on one GPU race on that array."""
+    args, params, B, L = _step_args(qkv, positions, table, seq_lens, k_cache, v_cache, kv_scale,
+                                     page_size, layer_kind, out, stream, q_norm_w, k_norm_w,
+                                     o_norm_w, max_seq_len, eps, q_scale, rope_base, work_groups)
+    st = lib().museattn_attn_step_noalloc(*args)
+    if st != OK:
+        raise MuseAttnError(st, "museattn_attn_step_noalloc")
     return out
 
 

@@ -1,6 +1,7 @@
 // Host side of libmuseattn: argument validation, the launch shape (a function
 // of host shapes only, so a call can be captured into a HIP graph), workspace
 // layout and the two launches.  See include/museattn.h for the contract.
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 
@@ -110,54 +111,17 @@ int check_shapes(int B, int L, int max_seq_len, int page_size, int layer_kind,
   return MUSEATTN_OK;
 }
 
-}  // namespace
-}  // namespace museattn
-
-using namespace museattn;
-
-extern "C" {
-
-int museattn_abi_version(void) { return MUSEATTN_ABI_VERSION; }
-
-const char *museattn_strerror(int status) {
-  switch (status) {
-    case MUSEATTN_OK: return "ok";
-    case MUSEATTN_ERR_NULL: return "a required pointer is null";
-    case MUSEATTN_ERR_PAGE_SIZE: return "page_size must be 1 or 64";
-    case MUSEATTN_ERR_LAYER_KIND: return "layer_kind must be MUSEATTN_FULL or MUSEATTN_SLIDING";
-    case MUSEATTN_ERR_SHAPE:
-      return "B, L, B * ceil(L / 16) (L > 8), max_seq_len, the plan's chunk count or num_rows "
-             "out of range";
-    case MUSEATTN_ERR_TABLE: return "table_stride < ceil(max_seq_len / page_size)";
-    case MUSEATTN_ERR_ALIGN: return "misaligned pointer (caches, qkv and weights need 16 bytes, out 8)";
-    case MUSEATTN_ERR_WORKSPACE: return "workspace too small or not 256-byte aligned";
-    case MUSEATTN_ERR_PARAM: return "kv_scale, eps, q_scale, rope_base or work_groups out of range";
-    case MUSEATTN_ERR_ALIAS:
-      return "a written buffer (out, k_cache, v_cache, workspace) overlaps another buffer";
-    case MUSEATTN_ERR_LAUNCH: return "kernel launch failed";
-    default: return "unknown status";
-  }
-}
-
-int museattn_work_groups(int B, int L, int max_seq_len, int layer_kind, const museattn_params *params) {
-  if (check_shapes(B, L, max_seq_len, 1, layer_kind, params) != MUSEATTN_OK) return 0;
-  return choose_work_groups(L, params->work_groups);
-}
-
-size_t museattn_workspace_bytes(int B, int L, int max_seq_len, int page_size, int layer_kind,
-                                const museattn_params *params) {
-  if (check_shapes(B, L, max_seq_len, page_size, layer_kind, params) != MUSEATTN_OK) return 0;
-  return layout(B, L, choose_work_groups(L, params->work_groups)).total;
-}
-
-int museattn_check_args(const void *qkv, const int32_t *positions, const int32_t *table,
-                        const int32_t *seq_lens, const void *k_cache, const void *v_cache,
-                        float kv_scale, int page_size, int layer_kind, const void *out, int B,
-                        int L, int table_stride, int max_seq_len, int64_t num_rows,
-                        const museattn_params *params, const void *workspace,
-                        size_t workspace_bytes) {
+// Host-side validation of a step's arguments (touches no device memory).
+// has_ws: the caller passes the workspace (else the library's static scratch
+// serves, and only its size is checked, by the caller of this function).
+int check_step_args(const void *qkv, const int32_t *positions, const int32_t *table,
+                    const int32_t *seq_lens, const void *k_cache, const void *v_cache,
+                    float kv_scale, int page_size, int layer_kind, const void *out, int B, int L,
+                    int table_stride, int max_seq_len, int64_t num_rows,
+                    const museattn_params *params, bool has_ws, const void *workspace,
+                    size_t workspace_bytes) {
   if (!qkv || !positions || !table || !seq_lens || !k_cache || !v_cache || !out || !params ||
-      !workspace)
+      (has_ws && !workspace))
     return MUSEATTN_ERR_NULL;
   if (!params->q_norm_w || !params->k_norm_w || !params->o_norm_w) return MUSEATTN_ERR_NULL;
   const int st = check_shapes(B, L, max_seq_len, page_size, layer_kind, params);
@@ -177,8 +141,8 @@ int museattn_check_args(const void *qkv, const int32_t *positions, const int32_t
       !(std::isfinite(params->eps) && params->eps >= 0.0f) || !std::isfinite(params->q_scale) ||
       !(std::isfinite(params->rope_base) && params->rope_base > 0.0f))
     return MUSEATTN_ERR_PARAM;
-  if (!aligned(workspace, 256) ||
-      workspace_bytes < museattn_workspace_bytes(B, L, max_seq_len, page_size, layer_kind, params))
+  if (has_ws && (!aligned(workspace, 256) ||
+                 workspace_bytes < layout(B, L, choose_work_groups(L, params->work_groups)).total))
     return MUSEATTN_ERR_WORKSPACE;
   // the buffers the step writes (out, the caches' new rows, the workspace)
   // must not overlap each other or anything the step reads: every work-group
@@ -193,7 +157,7 @@ int museattn_check_args(const void *qkv, const int32_t *positions, const int32_t
   const uint64_t T = (uint64_t)B * L;
   const Span written[4] = {span(out, T * HQ * D * 2), span(k_cache, (uint64_t)num_rows * ROW),
                            span(v_cache, (uint64_t)num_rows * ROW),
-                           span(workspace, workspace_bytes)};
+                           span(has_ws ? workspace : nullptr, has_ws ? workspace_bytes : 0)};
   const Span read[7] = {span(qkv, T * QKV_W * 2), span(positions, T * 4),
                         span(table, (uint64_t)B * table_stride * 4), span(seq_lens, (uint64_t)B * 4),
                         span(params->q_norm_w, D * 4), span(params->k_norm_w, D * 4),
@@ -207,17 +171,14 @@ int museattn_check_args(const void *qkv, const int32_t *positions, const int32_t
   return MUSEATTN_OK;
 }
 
-int museattn_attn_step_profiled(const void *qkv, const int32_t *positions, const int32_t *table,
-                                const int32_t *seq_lens, void *k_cache, void *v_cache,
-                                float kv_scale, int page_size, int layer_kind, void *out,
-                                void *stream, int B, int L, int table_stride, int max_seq_len,
-                                int64_t num_rows, const museattn_params *params, void *workspace,
-                                size_t workspace_bytes, void *attn_start_event,
-                                void *attn_end_event) {
-  const int st = museattn_check_args(qkv, positions, table, seq_lens, k_cache, v_cache, kv_scale,
-                                     page_size, layer_kind, out, B, L, table_stride, max_seq_len,
-                                     num_rows, params, workspace, workspace_bytes);
-  if (st != MUSEATTN_OK) return st;
+// Enqueues one validated step: the kernels read and write `ws` as the
+// workspace of museattn_workspace_bytes(...) bytes.
+int enqueue_step(const void *qkv, const int32_t *positions, const int32_t *table,
+                 const int32_t *seq_lens, void *k_cache, void *v_cache, float kv_scale,
+                 int page_size, int layer_kind, void *out, void *stream, int B, int L,
+                 int table_stride, int max_seq_len, int64_t num_rows,
+                 const museattn_params *params, void *workspace, void *attn_start_event,
+                 void *attn_end_event) {
   const Layout ly = layout(B, L, choose_work_groups(L, params->work_groups));
   char *ws = static_cast<char *>(workspace);
 
@@ -266,6 +227,105 @@ int museattn_attn_step_profiled(const void *qkv, const int32_t *positions, const
   return hipGetLastError() == hipSuccess ? MUSEATTN_OK : MUSEATTN_ERR_LAUNCH;
 }
 
+// The step's scratch for callers that cannot allocate device memory
+// (museattn_attn_step_noalloc): one fixed array per GPU, held until the
+// process ends.  In host code `scratch` names a host-side stand-in, never the
+// device memory: the kernels receive the address hipGetSymbolAddress returns
+// for the current device, looked up once per device and kept here (the only
+// state the library keeps between calls; it allocates nothing).
+constexpr int MAX_DEVICES = 64;
+static __device__ __align__(256) uint8_t scratch[MUSEATTN_STATIC_SCRATCH_BYTES];
+std::atomic<uintptr_t> scratch_addr[MAX_DEVICES];   // 0 until looked up
+
+// The device address of `scratch` on the device `stream` runs on (with that
+// device current during the lookup); MUSEATTN_ERR_LAUNCH if HIP cannot say.
+int scratch_for(hipStream_t stream, void **out) {
+  int cur = 0;
+  if (hipGetDevice(&cur) != hipSuccess) return MUSEATTN_ERR_LAUNCH;
+  int dev = cur;
+  if (stream != nullptr && hipStreamGetDevice(stream, &dev) != hipSuccess) return MUSEATTN_ERR_LAUNCH;
+  if (dev < 0 || dev >= MAX_DEVICES) return MUSEATTN_ERR_LAUNCH;
+  uintptr_t p = scratch_addr[dev].load(std::memory_order_acquire);
+  if (p == 0) {
+    if (dev != cur && hipSetDevice(dev) != hipSuccess) return MUSEATTN_ERR_LAUNCH;
+    void *ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (dev != cur) (void)hipSetDevice(cur);
+    if (e != hipSuccess || ptr == nullptr || !aligned(ptr, 256)) return MUSEATTN_ERR_LAUNCH;
+    p = (uintptr_t)ptr;
+    scratch_addr[dev].store(p, std::memory_order_release);   // a racing lookup stores the same
+  }
+  *out = reinterpret_cast<void *>(p);
+  return MUSEATTN_OK;
+}
+
+}  // namespace
+}  // namespace museattn
+
+using namespace museattn;
+
+extern "C" {
+
+int museattn_abi_version(void) { return MUSEATTN_ABI_VERSION; }
+
+const char *museattn_strerror(int status) {
+  switch (status) {
+    case MUSEATTN_OK: return "ok";
+    case MUSEATTN_ERR_NULL: return "a required pointer is null";
+    case MUSEATTN_ERR_PAGE_SIZE: return "page_size must be 1 or 64";
+    case MUSEATTN_ERR_LAYER_KIND: return "layer_kind must be MUSEATTN_FULL or MUSEATTN_SLIDING";
+    case MUSEATTN_ERR_SHAPE:
+      return "B, L, B * ceil(L / 16) (L > 8), max_seq_len, the plan's chunk count or num_rows "
+             "out of range";
+    case MUSEATTN_ERR_TABLE: return "table_stride < ceil(max_seq_len / page_size)";
+    case MUSEATTN_ERR_ALIGN: return "misaligned pointer (caches, qkv and weights need 16 bytes, out 8)";
+    case MUSEATTN_ERR_WORKSPACE: return "workspace too small or not 256-byte aligned";
+    case MUSEATTN_ERR_PARAM: return "kv_scale, eps, q_scale, rope_base or work_groups out of range";
+    case MUSEATTN_ERR_ALIAS:
+      return "a written buffer (out, k_cache, v_cache, workspace) overlaps another buffer";
+    case MUSEATTN_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int museattn_work_groups(int B, int L, int max_seq_len, int layer_kind, const museattn_params *params) {
+  if (check_shapes(B, L, max_seq_len, 1, layer_kind, params) != MUSEATTN_OK) return 0;
+  return choose_work_groups(L, params->work_groups);
+}
+
+size_t museattn_workspace_bytes(int B, int L, int max_seq_len, int page_size, int layer_kind,
+                                const museattn_params *params) {
+  if (check_shapes(B, L, max_seq_len, page_size, layer_kind, params) != MUSEATTN_OK) return 0;
+  return layout(B, L, choose_work_groups(L, params->work_groups)).total;
+}
+
+int museattn_check_args(const void *qkv, const int32_t *positions, const int32_t *table,
+                        const int32_t *seq_lens, const void *k_cache, const void *v_cache,
+                        float kv_scale, int page_size, int layer_kind, const void *out, int B,
+                        int L, int table_stride, int max_seq_len, int64_t num_rows,
+                        const museattn_params *params, const void *workspace,
+                        size_t workspace_bytes) {
+  return check_step_args(qkv, positions, table, seq_lens, k_cache, v_cache, kv_scale, page_size,
+                         layer_kind, out, B, L, table_stride, max_seq_len, num_rows, params, true,
+                         workspace, workspace_bytes);
+}
+
+int museattn_attn_step_profiled(const void *qkv, const int32_t *positions, const int32_t *table,
+                                const int32_t *seq_lens, void *k_cache, void *v_cache,
+                                float kv_scale, int page_size, int layer_kind, void *out,
+                                void *stream, int B, int L, int table_stride, int max_seq_len,
+                                int64_t num_rows, const museattn_params *params, void *workspace,
+                                size_t workspace_bytes, void *attn_start_event,
+                                void *attn_end_event) {
+  const int st = museattn_check_args(qkv, positions, table, seq_lens, k_cache, v_cache, kv_scale,
+                                     page_size, layer_kind, out, B, L, table_stride, max_seq_len,
+                                     num_rows, params, workspace, workspace_bytes);
+  if (st != MUSEATTN_OK) return st;
+  return enqueue_step(qkv, positions, table, seq_lens, k_cache, v_cache, kv_scale, page_size,
+                      layer_kind, out, stream, B, L, table_stride, max_seq_len, num_rows, params,
+                      workspace, attn_start_event, attn_end_event);
+}
+
 int museattn_attn_step(const void *qkv, const int32_t *positions, const int32_t *table,
                        const int32_t *seq_lens, void *k_cache, void *v_cache, float kv_scale,
                        int page_size, int layer_kind, void *out, void *stream, int B, int L,
@@ -275,6 +335,27 @@ int museattn_attn_step(const void *qkv, const int32_t *positions, const int32_t 
                                      page_size, layer_kind, out, stream, B, L, table_stride,
                                      max_seq_len, num_rows, params, workspace, workspace_bytes,
                                      nullptr, nullptr);
+}
+
+int museattn_attn_step_noalloc(const void *qkv, const int32_t *positions, const int32_t *table,
+                               const int32_t *seq_lens, void *k_cache, void *v_cache,
+                               float kv_scale, int page_size, int layer_kind, void *out,
+                               void *stream, int B, int L, int table_stride, int max_seq_len,
+                               int64_t num_rows, const museattn_params *params) {
+  const int st = check_step_args(qkv, positions, table, seq_lens, k_cache, v_cache, kv_scale,
+                                 page_size, layer_kind, out, B, L, table_stride, max_seq_len,
+                                 num_rows, params, false, nullptr, 0);
+  if (st != MUSEATTN_OK) return st;
+  if (layout(B, L, choose_work_groups(L, params->work_groups)).total > MUSEATTN_STATIC_SCRATCH_BYTES)
+    return MUSEATTN_ERR_WORKSPACE;
+  void *ws = nullptr;
+  const int sst = scratch_for(static_cast<hipStream_t>(stream), &ws);
+  if (sst != MUSEATTN_OK) return sst;
+  // Nothing in the scratch has to start at zero: the attention kernel writes
+  // the plan and every partial slot the combine kernel reads.
+  return enqueue_step(qkv, positions, table, seq_lens, k_cache, v_cache, kv_scale, page_size,
+                      layer_kind, out, stream, B, L, table_stride, max_seq_len, num_rows, params,
+                      ws, nullptr, nullptr);
 }
 
 namespace {
