@@ -36,7 +36,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 MFMA_F16_PEAK_TFLOPS = 2500.0
-OPROJ_GEMM_MIN_T = 160   # from this many tokens on the library runs the projection through hipBLASLt
+OPROJ_GEMM_MIN_T = 160   # from this many tokens on the library runs the projection as its LDS-tiled GEMM
 OPROJ_HIDDEN = 8192   # the decoder layer's model width (the page's [T, 8192] activations)
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "attn_kernel_decode_b32_full_ctx60k-100k_pmc.txt")
 ATTN_SOURCE = os.path.join(ROOT, "paged_fp8_kv_amd", "csrc", "attn_splitk.hip")
@@ -302,7 +302,8 @@ def main():
             ach, peak, unit = oflops / (o_avg * 1e-3) / 1e12, MFMA_F16_PEAK_TFLOPS, "TFLOP/s"
         else:
             ach, peak, unit = obytes / (o_avg * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s"
-        oproj = {"kernel": ("hipBLASLt bf16 GEMM (y = out . o^T, fp32 sums)" if w.T >= OPROJ_GEMM_MIN_T
+        oproj = {"kernel": ("gemm_kernel (y = out . o^T, LDS-tiled bf16 MFMA GEMM, fp32 sums)"
+                            if w.T >= OPROJ_GEMM_MIN_T
                             else "oproj_kernel (y = out . o^T, bf16 MFMA, fp32 sums)"),
                  "hidden": OPROJ_HIDDEN, "tokens": w.T, "bound": "mfma" if mfma_bound else "hbm",
                  "algorithmic_bytes_per_launch": obytes, "algorithmic_flops_per_launch": oflops,

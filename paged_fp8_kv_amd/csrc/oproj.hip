@@ -97,8 +97,8 @@ __global__ __launch_bounds__(256) void oproj_kernel(const uint16_t *__restrict__
   }
 }
 
-// From this many tokens on, the projection is a plain GEMM that hipBLASLt
-// runs faster than this kernel, which re-reads a once per 32 rows of o.
+// From this many tokens on, the LDS-tiled GEMM (oproj_gemm.hip) runs the
+// projection: this kernel re-reads a once per 32 rows of o.
 #ifndef MUSEATTN_OPROJ_GEMM_MIN_T
 #define MUSEATTN_OPROJ_GEMM_MIN_T 160
 #endif
@@ -106,7 +106,10 @@ constexpr int OP_GEMM_MIN_T = MUSEATTN_OPROJ_GEMM_MIN_T;
 
 void launch_oproj(const uint16_t *a, const uint16_t *o, uint16_t *y, int T, int N,
                   hipStream_t stream) {
-  if (T >= OP_GEMM_MIN_T && gemm_oproj(a, o, y, T, N, stream)) return;
+  if (T >= OP_GEMM_MIN_T) {
+    gemm_oproj(a, o, y, T, N, stream);
+    return;
+  }
   int passes = (T + OP_TOK - 1) / OP_TOK;
   passes = passes < OP_MAX_PASS_GROUPS ? passes : OP_MAX_PASS_GROUPS;
   hipLaunchKernelGGL(oproj_kernel, dim3(N / OP_ROWS, passes), dim3(256), 0, stream, a, o, y, T, N);

@@ -32,12 +32,16 @@ def _need_gpu():
 
 @pytest.mark.parametrize("T,hidden", [(1, 64), (7, 8192), (32, 8192), (33, 1088), (64, 8192),
                                       (65, 64), (100, 2048), (129, 1088), (159, 1088),
-                                      (160, 8192), (256, 8192), (753, 8192), (1024, 64)])
+                                      (160, 8192), (256, 8192), (753, 8192), (1024, 64),
+                                      (1000, 1088), (2048, 8192), (13100, 1088)])
 def test_oproj_alone(T, hidden):
-    """Up to 159 tokens the library's kernel runs (32 rows of o per work-group,
+    """Up to 159 tokens the register kernel runs (32 rows of o per work-group,
     64-token passes: T 33, 65, 100, 129 and 159 end inside a pass); from 160 on
-    the hipBLASLt GEMM (T 159 and 160 sit on either side of the switch, hidden
-    64 is its smallest shape)."""
+    the LDS-tiled GEMM (T 159 and 160 sit on either side of the switch).  The
+    GEMM's tiles: 128 x 64 (T 160, 256; T 1000 and hidden 1088, whose last
+    feature and token tiles are partial; hidden 64, half a tile), 128 x 128
+    (T 753) and 256 x 128 (T 2048; T 13100 with hidden 1088: partial tiles
+    on both axes)."""
     a = W.oproj_input(70 + T, T)
     o = W.oproj_weight(71, hidden)
     y = torch.empty(T, hidden, dtype=torch.bfloat16, device="cuda")
@@ -88,26 +92,23 @@ def test_step_then_oproj(case):
     compare_out(y.float().cpu().numpy(), want, f"{name} y")
 
 
-@pytest.mark.parametrize("T", [32, 753])
+@pytest.mark.parametrize("T", [32, 753, 2048])
 def test_oproj_graph_replays_match_eager(T):
-    """The projection captured into a HIP graph -- the library's kernel at 32
-    tokens, the hipBLASLt GEMM at 753 -- gives the eager call's bytes on every
-    replay, with eager calls in between."""
+    """The projection captured into a HIP graph on its first call of the shape
+    (the library keeps nothing between calls, so nothing has to be set up
+    first) -- the register kernel at 32 tokens, the GEMM at 753 and 2048 --
+    gives the eager call's bytes on every replay, with eager calls in between."""
     a = W.oproj_input(90 + T, T).cuda()
     o = W.oproj_weight(91, 8192).cuda()
     y = torch.empty(T, 8192, dtype=torch.bfloat16, device="cuda")
-    P.oproj(a, o, y)   # first call of the shape: makes the plan outside the capture
     torch.cuda.synchronize()
-    eager = y.clone()
     g = torch.cuda.CUDAGraph()
-    s = torch.cuda.Stream()
-    s.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(s):
-        P.oproj(a, o, y)   # warm-up on the capture stream
-    torch.cuda.current_stream().wait_stream(s)
-    torch.cuda.synchronize()
     with torch.cuda.graph(g):
         P.oproj(a, o, y)
+    y.zero_()
+    P.oproj(a, o, y)   # the eager result
+    torch.cuda.synchronize()
+    eager = y.clone()
     for i in range(3):
         y.zero_()
         torch.cuda.synchronize()
