@@ -88,53 +88,170 @@ def read_traffic(bytes_per_launch_alg):
         return None
 
 
-def cpu_baseline(w, sample_requests: int, sample_tokens: int):
-    """The oracle (as it stands) on a sample of the workload's requests; for a
-    prefill block, on evenly spaced block tokens of request 0."""
+def _oracle_job(job, barrier, results, index):
+    """One process of the CPU baseline: draws its share of the workload's
+    inputs (not timed), waits at the barrier for the other processes, then
+    times the oracle (unchanged) on that share with `blas_threads` BLAS
+    threads and puts (index, seconds) on the results queue."""
+    cid, pool_rows, requests, tokens, blas_threads = job
+    from threadpoolctl import threadpool_limits
     import numpy as np
     from oracle import museattn_oracle as O
     from paged_fp8_kv_amd import workloads as W
 
-    req = list(range(min(sample_requests, w.B))) if w.L <= 8 else [0]
-    sub = w.subset(req)
-    tokens = None
-    if w.L > 8:
-        tokens = sorted({int(x) for x in np.linspace(0, w.L - 1, min(sample_tokens, w.L))})
-    log(f"cpu_baseline: building the oracle's view of requests {req[0]}..{req[-1]}")
-    kp = W.LogicalPool(sub, range(sub.B), "k")
-    vp = W.LogicalPool(sub, range(sub.B), "v")
-    threads = 1
+    with threadpool_limits(blas_threads):
+        w = W.config(cid, pool_rows)
+        sub = w.subset(requests)
+        kp, vp = W.LogicalPool.pair(sub, range(sub.B))
+        barrier.wait(timeout=600)
+        t0 = time.perf_counter()
+        O.attn_step(sub.qkv.float().numpy(), sub.positions, sub.table, kp, vp, B=sub.B, L=sub.L,
+                    page_size=sub.page_size, layer_kind=sub.layer_kind, kv_scale=sub.kv_scale,
+                    w_q=sub.w_q, w_k=sub.w_k, w_o=sub.w_o, eps=float(np.float32(1e-6)),
+                    q_scale=float(np.float32(5.473)), tokens=tokens)
+        results.put((index, time.perf_counter() - t0))
+
+
+def _run_oracle_jobs(jobs):
+    """Each job in its own spawned process (fresh interpreters: no GPU state is
+    inherited), all released together; returns the per-process seconds."""
+    import multiprocessing as mp
+    ctx = mp.get_context("spawn")
+    barrier, results = ctx.Barrier(len(jobs)), ctx.Queue()
+    procs = [ctx.Process(target=_oracle_job, args=(job, barrier, results, i))
+             for i, job in enumerate(jobs)]
+    for p in procs:
+        p.start()
+    out = {}
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:
-        pass
-    t0 = time.perf_counter()
-    O.attn_step(sub.qkv.float().numpy(), sub.positions, sub.table, kp, vp, B=sub.B, L=sub.L,
-                page_size=sub.page_size, layer_kind=sub.layer_kind, kv_scale=sub.kv_scale,
-                w_q=sub.w_q, w_k=sub.w_k, w_o=sub.w_o, eps=float(np.float32(1e-6)),
-                q_scale=float(np.float32(5.473)), tokens=tokens)
-    dt = time.perf_counter() - t0
+        for _ in jobs:
+            i, sec = results.get(timeout=900)
+            out[i] = sec
+    finally:
+        for p in procs:
+            p.join(timeout=60)
+            if p.is_alive():
+                p.kill()
+    return [out[i] for i in range(len(jobs))]
+
+
+def _step_fraction(w, requests, tokens):
+    """The share of the step's work (K+V bytes; attention FLOPs for a prefill
+    block) that the oracle does on these requests (and block tokens)."""
+    import numpy as np
     if tokens is None:
-        frac = sub.kv_bytes / w.kv_bytes
-        what = f"requests 0..{req[-1]} ({sub.B} of {w.B}"
+        return w.subset(requests).kv_bytes / w.kv_bytes
+    p = w.positions[tokens].astype(np.int64)
+    keys = p + 1 if w.layer_kind == 0 else np.minimum(p + 1, 2048)
+    return float(keys.sum()) * 16 * 64 * 4 / w.attn_flops
+
+
+def cpu_baseline(w, cid, pool_rows, sample_requests: int, sample_tokens: int, max_procs: int):
+    """The oracle (as it stands, float64 numpy) on the host cores: a sample of
+    the workload's requests (for a prefill block, evenly spaced block tokens
+    of request 0) split over one spawned process per core, one BLAS thread
+    each, started together after each has drawn its inputs; and the same
+    oracle on one thread (one process, one BLAS thread) on a smaller sample.
+    Both are scaled to one step by the share of the step's work they did."""
+    import numpy as np
+
+    avail = len(os.sched_getaffinity(0))
+    procs = max(1, min(max_procs, avail))
+    if w.L <= 8:
+        req = list(range(min(sample_requests, w.B)))
+        groups = [req[i::procs] for i in range(procs) if req[i::procs]]
+        jobs = [(cid, pool_rows, g, None, 1) for g in groups]
+        one = (cid, pool_rows, req[:1], None, 1)
+        what = f"requests 0..{req[-1]} ({len(req)} of {w.B})"
+        frac = _step_fraction(w, req, None)
+        frac1 = _step_fraction(w, req[:1], None)
     else:
-        p = sub.positions[tokens].astype(np.int64)
-        keys = p + 1 if w.layer_kind == 0 else np.minimum(p + 1, 2048)
-        frac = float(keys.sum()) * 16 * 64 * 4 / w.attn_flops
-        what = (f"{len(tokens)} evenly spaced block tokens of request 0 (all {w.L} new rows "
-                f"written and the keys they see dequantised once")
-    step_s = dt / frac
-    log(f"cpu_baseline: {dt:.2f} s for {sub.kv_bytes / 1e6:.1f} MB of K+V -> {step_s:.2f} s/step")
-    if tokens is None:
-        value, unit = round(w.kv_bytes / step_s / 1e9, 4), "GB/s"
+        toks = sorted({int(x) for x in np.linspace(0, w.L - 1, min(sample_tokens, w.L))})
+        groups = [toks[i::procs] for i in range(procs) if toks[i::procs]]
+        jobs = [(cid, pool_rows, [0], g, 1) for g in groups]
+        one = (cid, pool_rows, [0], toks[::max(1, len(toks) // 8)], 1)
+        what = f"{len(toks)} evenly spaced block tokens of request 0"
+        frac = _step_fraction(w, [0], toks)
+        frac1 = _step_fraction(w, [0], one[3])
+    log(f"cpu_baseline: {what} over {len(jobs)} processes; one-thread run on a smaller sample")
+    wall = max(_run_oracle_jobs(jobs))
+    t1 = _run_oracle_jobs([one])[0]
+    step_s, step1_s = wall / frac, t1 / frac1
+    log(f"cpu_baseline: {len(jobs)} processes {wall:.2f} s -> {step_s:.3f} s/step; "
+        f"one thread {t1:.2f} s -> {step1_s:.3f} s/step")
+    if w.L <= 8:
+        conv, unit = (lambda sec: round(w.kv_bytes / sec / 1e9, 4)), "GB/s"
     else:
-        value, unit = round(w.attn_flops / step_s / 1e12, 6), "TFLOP/s"
-    return {"value": value, "unit": unit, "cores": int(threads),
-            "kind": "oracle",
+        conv, unit = (lambda sec: round(w.attn_flops / sec / 1e12, 6)), "TFLOP/s"
+    return {"value": conv(step_s), "unit": unit, "cores": len(jobs), "kind": "oracle",
+            "threads_per_process": 1, "host_cores": os.cpu_count(), "available_cores": avail,
+            "s_per_step": round(step_s, 4),
+            "one_thread": {"value": conv(step1_s), "s_per_step": round(step1_s, 4),
+                           "sample_fraction": round(frac1, 5)},
             "sample": f"{what}, {frac * 100:.2f}% of the step's "
-                      f"{'K+V bytes' if tokens is None else 'attention FLOPs'}), float64 numpy "
-                      f"oracle, {dt:.2f} s; scaled to one step ({step_s:.2f} s/step)"}
+                      f"{'K+V bytes' if w.L <= 8 else 'attention FLOPs'}; float64 numpy oracle "
+                      f"in {len(jobs)} processes of one BLAS thread each (slowest {wall:.2f} s), "
+                      f"scaled to one step"}
+
+
+TS_SLOTS = 12   # per attention work-group in the instrumented build (device_common.h)
+TS_NAMES = ("entry", "plan", "setup", "stream", "partial", "exit")
+
+
+def phase_report(w, step, ws, G, reps):
+    """Per-phase times of the step from the instrumented library (built with
+    MUSEATTN_PHASE_TIMES): each attention work-group stamps the GPU's 100 MHz
+    real-time counter at entry, when its plan is ready, when its first
+    segment's loads and set-up are done, when that segment's key chunks are
+    done, when its partials are written and at exit; each combine work-group
+    at entry and exit.  All times are relative to the first attention entry;
+    medians over `reps` eager steps."""
+    import numpy as np
+    import torch
+
+    T = w.B * w.L
+    al = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    ts_bytes = al((G * TS_SLOTS + 2 * T * 16) * 8)
+    region = ws[ws.numel() - ts_bytes:]
+    rows = []
+    for _ in range(reps):
+        region.zero_()
+        torch.cuda.synchronize()
+        step()
+        torch.cuda.synchronize()
+        v = region.view(torch.int64).cpu().numpy()
+        att = v[:G * TS_SLOTS].reshape(G, TS_SLOTS)
+        comb = v[G * TS_SLOTS:G * TS_SLOTS + 2 * T * 16].reshape(-1, 2)
+        comb = comb[(comb[:, 0] > 0) & (comb[:, 1] > 0)]
+        t0 = att[:, 0].min()
+        us = lambda x: (x - t0) / 100.0  # noqa: E731  (100 MHz counter -> us)
+        act = att[att[:, 6] > 0]
+        r = {"entry_first": 0.0, "entry_last": float(us(att[:, 0].max())),
+             "plan_median": float(np.median(act[:, 1] - act[:, 0]) / 100.0),
+             "setup_median": float(np.median(act[:, 2] - act[:, 1]) / 100.0),
+             "setup_issue_median": float(np.median(act[:, 7] - act[:, 1]) / 100.0),
+             "setup_loads_median": float(np.median(act[:, 8] - act[:, 7]) / 100.0),
+             "setup_q_median": float(np.median(act[:, 9] - act[:, 8]) / 100.0),
+             "setup_barrier_median": float(np.median(act[:, 2] - act[:, 9]) / 100.0),
+             "stream_median": float(np.median(act[:, 3] - act[:, 2]) / 100.0),
+             "partial_median": float(np.median(act[:, 4] - act[:, 3]) / 100.0),
+             "rest_median": float(np.median(act[:, 5] - act[:, 4]) / 100.0),
+             "attn_exit_last": float(us(att[:, 5].max())),
+             "combine_entry_first": float(us(comb[:, 0].min())),
+             "combine_exit_last": float(us(comb[:, 1].max())),
+             "active_work_groups": int(len(act)), "combine_work_groups": int(len(comb))}
+        crit = act[np.argmax(act[:, 5])]
+        r["critical_wg"] = {n: float(us(crit[i])) for i, n in enumerate(TS_NAMES)}
+        r["critical_wg"]["segments"] = int(crit[6])
+        rows.append(r)
+    keys = [k for k in rows[0] if k != "critical_wg" and not k.endswith("work_groups")]
+    out = {k: round(float(np.median([r[k] for r in rows])), 2) for k in keys}
+    out["active_work_groups"] = rows[0]["active_work_groups"]
+    out["combine_work_groups"] = rows[0]["combine_work_groups"]
+    mid = sorted(rows, key=lambda r: r["attn_exit_last"])[len(rows) // 2]
+    out["critical_wg_of_median_step"] = {k: round(v, 2) for k, v in mid["critical_wg"].items()}
+    out["reps"] = reps
+    return out
 
 
 def main():
@@ -152,7 +269,9 @@ def main():
                     help="override the pool size in rows (0 = the workload's own)")
     ap.add_argument("--cold-reps", type=int, default=200,
                     help="graph replays timed one by one after a 1 GiB cache flush")
-    ap.add_argument("--cpu-sample", type=int, default=16, help="requests the oracle times")
+    ap.add_argument("--cpu-sample", type=int, default=32, help="requests the oracle times")
+    ap.add_argument("--cpu-procs", type=int, default=16,
+                    help="most oracle processes (one per host core of the GPU's share)")
     ap.add_argument("--cpu-sample-tokens", type=int, default=96,
                     help="block tokens the oracle times (prefill blocks)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -166,7 +285,13 @@ def main():
                          "(bf16 o [8192, 1024]); reported in the 'oproj' field")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="run a 1 GiB device copy first (PMC calibration runs)")
+    ap.add_argument("--phases", action="store_true",
+                    help="load the instrumented library (per-phase timestamps) and print a "
+                         "phase breakdown of the step instead of the benchmark line")
     args = ap.parse_args()
+    if args.phases:   # before the package is imported: it reads MUSEATTN_LIB once
+        os.environ["MUSEATTN_LIB"] = os.path.join(ROOT, "paged_fp8_kv_amd",
+                                                  "libmuseattn_phases.so")
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the step "
@@ -226,6 +351,16 @@ def main():
         step()
     torch.cuda.synchronize()
     log(f"warmup {args.warmup} steps done")
+
+    if args.phases:
+        G = P.work_groups(w.B, w.L, w.max_seq_len, w.layer_kind, args.work_groups)
+        rep = phase_report(w, step, ws, G, max(args.steps, 5))
+        log("phases (us from the first attention work-group's entry): " + json.dumps(rep))
+        print(json.dumps({"phases": rep, "library": os.path.basename(P.LIB_PATH),
+                          "config": {"workload": w.name, "B": w.B, "L": w.L,
+                                     "layer": "full" if w.layer_kind == 0 else "sliding",
+                                     "page_size": w.page_size, "work_groups": G}}), flush=True)
+        return
 
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(args.steps)]
@@ -394,7 +529,8 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, args.cpu_sample, args.cpu_sample_tokens)
+        cpu = cpu_baseline(w, args.config, args.pool_rows or None, args.cpu_sample,
+                           args.cpu_sample_tokens, args.cpu_procs)
 
     line = {
         "metric": metric,

@@ -14,7 +14,9 @@ import ctypes
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libmuseattn.so")
+# MUSEATTN_LIB may name another build of the library (the instrumented
+# libmuseattn_phases.so that bench.py --phases loads)
+LIB_PATH = os.environ.get("MUSEATTN_LIB") or os.path.join(HERE, "libmuseattn.so")
 
 FULL, SLIDING = 0, 1
 HQ, HKV, D = 16, 2, 64

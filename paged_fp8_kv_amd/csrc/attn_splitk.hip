@@ -671,7 +671,7 @@ struct Lds {
 // head in slot `slot`.  The 8 waves take interleaved chunks and both KV heads.
 template <int NBUF>
 __device__ __forceinline__ void process_segment(const StepArgs &a, int b, const KeyRange &r, int x,
-                                                int y, int slot, Lds<0> &sh) {
+                                                int y, int slot, Lds<0> &sh, bool first) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int n = lane & 15, j = lane >> 4;
   const float qmul = a.kv_scale * (LOG2E / 8.0f);
@@ -692,6 +692,7 @@ __device__ __forceinline__ void process_segment(const StepArgs &a, int b, const 
   const f32x4 wv[4] = {w4[0], w4[1], w4[2], w4[3]};
   const RowIn rin = load_row_in(a, b);
   __builtin_amdgcn_sched_barrier(0);
+  stamp(a, TS_ISSUED, first);
   // the token's RoPE (cos, sin) pairs (L = 1), computed while the loads fly
   float2 csv = make_float2(1.0f, 0.0f);
   if (a.sliding && tid < 32) csv = rope_cs(pos[0], tid);
@@ -702,6 +703,7 @@ __device__ __forceinline__ void process_segment(const StepArgs &a, int b, const 
     __syncthreads();
   }
   store_table(a, tin, sh.lrows);
+  stamp(a, TS_TABLE, first);
 
   // per-token key ranges: the causal bound is the token's position p, the
   // window (sliding layers) starts 2047 keys before it
@@ -728,8 +730,10 @@ __device__ __forceinline__ void process_segment(const StepArgs &a, int b, const 
     owned |= in ? 1u << jt : 0u;
   }
   if (owned && wave < 4) write_new_rows(a, b, owned, pos, sh.cs, rin);
+  stamp(a, TS_QREADY, first);
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
   __syncthreads();
+  stamp(a, TS_SETUP, first);
 
   for (int pc = 0; pc < npieces; ++pc) {
     const int px = piece_x(pc), py = piece_x(pc + 1);
@@ -774,6 +778,7 @@ __device__ __forceinline__ void process_segment(const StepArgs &a, int b, const 
     }
   }
 
+  stamp(a, TS_STREAM, first);
   // Lane (n, j) holds O^T of head n at V-row bytes 8(4j + r) + mt, r < 4: KV
   // head j/2, dims 32(j%2) + 8r + mt.  Only lanes whose KV head is head n's
   // own hold meaningful values.
@@ -816,6 +821,7 @@ __device__ __forceinline__ void process_segment(const StepArgs &a, int b, const 
     a.part_ml[e * 2] = M;
     a.part_ml[e * 2 + 1] = lt;
   }
+  stamp(a, TS_PARTIAL, first);
 }
 
 // Blocks: the q of one (token, head) column in the lane layout of the block
@@ -869,7 +875,7 @@ __device__ __forceinline__ void q_values2(const StepArgs &a, const QIn2 &in, con
 template <int MODE>
 __device__ __forceinline__ void process_segment_block(const StepArgs &a, int b, int blk,
                                                       const KeyRange &r, int x, int y, int slot,
-                                                      Lds<MODE> &sh) {
+                                                      Lds<MODE> &sh, bool first) {
   constexpr bool VERIFY = MODE == 2;
   constexpr int NR = MUSEATTN_BLOCK_PREFETCH;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -953,6 +959,7 @@ __device__ __forceinline__ void process_segment_block(const StepArgs &a, int b, 
     }
   }
 
+  stamp(a, TS_ISSUED, first);
   // RoPE (cos, sin) of the unit's tokens (512 threads: up to 16 tokens x 32
   // pairs), computed while the loads fly
   float2 csv = make_float2(1.0f, 0.0f);
@@ -964,6 +971,7 @@ __device__ __forceinline__ void process_segment_block(const StepArgs &a, int b, 
     __syncthreads();
   }
   store_table(a, tin, sh.lrows);
+  stamp(a, TS_TABLE, first);
 
   f16x8 qf[2][2];
   BlockState st;
@@ -1011,7 +1019,9 @@ __device__ __forceinline__ void process_segment_block(const StepArgs &a, int b, 
     if (owned && wave < 4) write_new_rows(a, b, owned, pos, sh.cs, rin);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
   }
+  stamp(a, TS_QREADY, first);
   __syncthreads();   // the row ids (and verify's new rows) are in place
+  stamp(a, TS_SETUP, first);
 
   for (int pc = 0; pc < npieces; ++pc) {
     const int px = piece_x(pc), py = piece_x(pc + 1);
@@ -1071,6 +1081,7 @@ __device__ __forceinline__ void process_segment_block(const StepArgs &a, int b, 
     }
   }
 
+  stamp(a, TS_STREAM, first);
   float lsum[2];
 #pragma unroll
   for (int c = 0; c < 2; ++c) lsum[c] = st.o[4][c][0];
@@ -1129,6 +1140,7 @@ __device__ __forceinline__ void process_segment_block(const StepArgs &a, int b, 
         *reinterpret_cast<f32x4 *>(a.part_o + e * D + 16 * dt + 4 * j) = st.o[dt][c];
     }
   }
+  stamp(a, TS_PARTIAL, first);
 }
 
 // The attention kernel.  Every work-group derives the same plan from the
@@ -1145,6 +1157,7 @@ __global__ __launch_bounds__(THREADS, 2) void attn_kernel(StepArgs a) {
   __shared__ __attribute__((aligned(16))) Lds<MODE> sh;
   constexpr int MAXU = Lds<MODE>::MAXU;
   const int tid = threadIdx.x;
+  stamp(a, TS_ENTRY);
   const int NU = a.nunits;
 
   // chunk-count prefix sums over the plan units (RPT per thread)
@@ -1200,6 +1213,7 @@ __global__ __launch_bounds__(THREADS, 2) void attn_kernel(StepArgs a) {
     if (tid == 0) sh.pref[NU] = total;
   }
   __syncthreads();
+  stamp(a, TS_PLAN);
   // Cost space: unit u occupies seg_cost units (its segment start-up, in
   // chunk-equivalents), then its chunks, then end_cost units (the new rows
   // the holder of its last chunk writes), so unit u starts at cost Q_u =
@@ -1215,7 +1229,11 @@ __global__ __launch_bounds__(THREADS, 2) void attn_kernel(StepArgs a) {
     for (int i = tid; i <= NU; i += THREADS) a.plan[i] = sh.pref[i];
     if (tid == 0) a.plan[NU + 1] = G;
   }
-  if (w >= G) return;   // uniform over the work-group
+  if (w >= G) {   // uniform over the work-group
+    stamp_count(a, TS_SEGMENTS, 0);
+    stamp(a, TS_EXIT);
+    return;
+  }
   const int64_t cb = (int64_t)w * Ct / G, ce = (int64_t)(w + 1) * Ct / G;
   auto cost_of = [&](int uu) { return (int64_t)sh.pref[uu] + (int64_t)uu * per; };
   int u = 0;
@@ -1226,6 +1244,7 @@ __global__ __launch_bounds__(THREADS, 2) void attn_kernel(StepArgs a) {
       if (cost_of(mid) <= cb) u = mid; else hi = mid - 1;
     }
   }
+  int nsegs = 0;
   for (; u < NU && cost_of(u) < ce; ++u) {
     const int64_t q0 = cost_of(u) + pen;            // cost of chunk 0 of unit u
     const int64_t nb = sh.pref[u + 1] - sh.pref[u];
@@ -1237,10 +1256,13 @@ __global__ __launch_bounds__(THREADS, 2) void attn_kernel(StepArgs a) {
     int b, blk;
     unit_of(a, u, b, blk);
     if constexpr (MODE == 0)
-      process_segment<NBUF>(a, b, r, x, y, w + u, sh);
+      process_segment<NBUF>(a, b, r, x, y, w + u, sh, nsegs == 0);
     else
-      process_segment_block<MODE>(a, b, blk, r, x, y, w + u, sh);
+      process_segment_block<MODE>(a, b, blk, r, x, y, w + u, sh, nsegs == 0);
+    ++nsegs;
   }
+  stamp_count(a, TS_SEGMENTS, (uint64_t)nsegs);
+  stamp(a, TS_EXIT);
 }
 
 void launch_attn(const StepArgs &a, hipStream_t stream) {

@@ -25,6 +25,7 @@ __global__ __launch_bounds__(256) void combine_kernel(StepArgs a) {
   __shared__ float sm_m[16], sm_l[16];
   __shared__ __attribute__((aligned(16))) float sm_o[16][D];
 
+  stamp_combine(a, 0);
   const int th = blockIdx.x;          // t * 16 + h
   const int t = th / HQ, h = th % HQ;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -131,12 +132,14 @@ __global__ __launch_bounds__(256) void combine_kernel(StepArgs a) {
     const float y = av / sqrtf(ms2 + a.eps) * wo;
     a.out[(size_t)t * (HQ * D) + h * D + d] = f32_to_bf16_bits(y / (1.0f + expf(-g)));
   }
+  stamp_combine(a, 1);
 }
 
 // Prefill merge: work-group t = token t; lane group hg = lane / 16 of wave w
 // takes head h = 4w + hg, lane dq = lane % 16 its dims 4dq..4dq+3.  All heads
 // of a token share its unit's slots.
 __global__ __launch_bounds__(256) void combine_tokens_kernel(StepArgs a) {
+  stamp_combine(a, 0);
   const int t = blockIdx.x;
   const int tid = threadIdx.x, h = tid >> 4, dq = tid & 15;
   const int b = t / a.L, jl = t % a.L;
@@ -200,6 +203,7 @@ __global__ __launch_bounds__(256) void combine_tokens_kernel(StepArgs a) {
   }
   *reinterpret_cast<uint2 *>(a.out + (size_t)t * (HQ * D) + h * D + 4 * dq) =
       uint2{packed[0], packed[1]};
+  stamp_combine(a, 1);
 }
 
 #ifndef MUSEATTN_TOKENS_COMBINE_MIN_B

@@ -54,7 +54,46 @@ struct StepArgs {
   // Plan units: request b's block tokens in groups of tb (unit u = b * nblk +
   // blk holds tokens blk*tb ..); one group per request (tb = L) up to L = 8.
   int tb, nblk, nunits;
+  uint64_t *ts;            // phase timestamps (MUSEATTN_PHASE_TIMES builds), else null
 };
+
+// Per-phase timestamps, compiled in only with MUSEATTN_PHASE_TIMES (an
+// instrumented build of the library): thread 0 of a work-group stores the
+// GPU's 100 MHz real-time counter, or a count, into one slot of its row of
+// a.ts with an ordinary vector store.  Attention work-group w owns slots
+// [w * TS_SLOTS, (w + 1) * TS_SLOTS); combine work-group c owns the two
+// slots at work_groups * TS_SLOTS + 2c (entry, exit).
+constexpr int TS_SLOTS = 12;
+enum TsSlot {
+  TS_ENTRY = 0,      // first instruction
+  TS_PLAN = 1,       // the plan (prefix sums over the units) is in LDS
+  TS_SETUP = 2,      // first segment: loads returned, row ids and q in place
+  TS_STREAM = 3,     // first segment: every key chunk processed
+  TS_PARTIAL = 4,    // first segment: partials written
+  TS_EXIT = 5,       // last instruction
+  TS_SEGMENTS = 6,   // segments processed (a count)
+  TS_ISSUED = 7,     // first segment: its batch of loads issued
+  TS_TABLE = 8,      // first segment: its row ids stored in LDS (the loads are back)
+  TS_QREADY = 9      // first segment: q operands (and any new rows) done, before the barrier
+};
+#ifdef MUSEATTN_PHASE_TIMES
+__device__ __forceinline__ void stamp(const StepArgs &a, int slot, bool on = true) {
+  if (on && threadIdx.x == 0)
+    a.ts[(size_t)blockIdx.x * TS_SLOTS + slot] = __builtin_amdgcn_s_memrealtime();
+}
+__device__ __forceinline__ void stamp_count(const StepArgs &a, int slot, uint64_t v) {
+  if (threadIdx.x == 0) a.ts[(size_t)blockIdx.x * TS_SLOTS + slot] = v;
+}
+__device__ __forceinline__ void stamp_combine(const StepArgs &a, int which) {
+  if (threadIdx.x == 0)
+    a.ts[(size_t)a.work_groups * TS_SLOTS + 2 * (size_t)blockIdx.x + which] =
+        __builtin_amdgcn_s_memrealtime();
+}
+#else
+__device__ __forceinline__ void stamp(const StepArgs &, int, bool = true) {}
+__device__ __forceinline__ void stamp_count(const StepArgs &, int, uint64_t) {}
+__device__ __forceinline__ void stamp_combine(const StepArgs &, int) {}
+#endif
 
 // Request and token group of plan unit u.
 __device__ __forceinline__ void unit_of(const StepArgs &a, int u, int &b, int &blk) {

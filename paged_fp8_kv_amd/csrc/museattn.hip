@@ -28,7 +28,7 @@ int choose_work_groups(int L, int requested) {
 
 struct Layout {
   int work_groups;
-  size_t plan_off, ml_off, o_off, total;
+  size_t plan_off, ml_off, o_off, ts_off, total;
 };
 
 // Plan units: up to 8 block tokens a request is one unit; beyond (prefill)
@@ -46,7 +46,13 @@ Layout layout(int B, int L, int work_groups) {
   ly.plan_off = 0;
   ly.ml_off = ly.plan_off + al((units + 2) * sizeof(int));
   ly.o_off = ly.ml_off + al(slots * tb * HQ * 2 * sizeof(float));
-  ly.total = ly.o_off + al(slots * tb * HQ * D * sizeof(float));
+  ly.ts_off = ly.o_off + al(slots * tb * HQ * D * sizeof(float));
+  ly.total = ly.ts_off;
+#ifdef MUSEATTN_PHASE_TIMES
+  // the timestamps at the end: TS_SLOTS per attention work-group, then two
+  // per combine work-group (at most one per token and head)
+  ly.total += al(((size_t)work_groups * TS_SLOTS + 2 * (size_t)B * L * HQ) * sizeof(uint64_t));
+#endif
   return ly;
 }
 
@@ -216,6 +222,11 @@ int enqueue_step(const void *qkv, const int32_t *positions, const int32_t *table
   a.tb = unit_tokens(L);
   a.nblk = units_per_request(L);
   a.nunits = B * a.nblk;
+#ifdef MUSEATTN_PHASE_TIMES
+  a.ts = reinterpret_cast<uint64_t *>(ws + ly.ts_off);
+#else
+  a.ts = nullptr;
+#endif
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();   // clear an error left by earlier, unrelated calls
