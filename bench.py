@@ -20,7 +20,10 @@ Prints ONE JSON line on stdout (progress goes to stderr):
               flush: median, p10, p90, bootstrap 95% interval of the median,
               and the replay time of a one-kernel graph (launch cost, not
               subtracted)
-  cpu_baseline  the CPU oracle on a sample of the same workload
+  gather_probe  the step's K/V row gather alone (full-layer workloads): the
+              attention kernel's ceiling on this memory system
+  cpu_baseline  the CPU oracle on the same workload, one process per host core,
+              and on one thread
 """
 from __future__ import annotations
 
@@ -226,6 +229,7 @@ def phase_report(w, step, ws, G, reps):
         t0 = att[:, 0].min()
         us = lambda x: (x - t0) / 100.0  # noqa: E731  (100 MHz counter -> us)
         act = att[att[:, 6] > 0]
+        two = att[att[:, 6] > 1]   # work-groups with a second segment
         r = {"entry_first": 0.0, "entry_last": float(us(att[:, 0].max())),
              "plan_median": float(np.median(act[:, 1] - act[:, 0]) / 100.0),
              "setup_median": float(np.median(act[:, 2] - act[:, 1]) / 100.0),
@@ -234,6 +238,10 @@ def phase_report(w, step, ws, G, reps):
              "setup_q_median": float(np.median(act[:, 9] - act[:, 8]) / 100.0),
              "setup_barrier_median": float(np.median(act[:, 2] - act[:, 9]) / 100.0),
              "stream_median": float(np.median(act[:, 3] - act[:, 2]) / 100.0),
+             "second_segment_setup_median": (float(np.median(two[:, 11] - two[:, 10]) / 100.0)
+                                             if len(two) else None),
+             "first_segment_setup_same_wgs_median": (float(np.median(two[:, 2] - two[:, 1]) / 100.0)
+                                                     if len(two) else None),
              "partial_median": float(np.median(act[:, 4] - act[:, 3]) / 100.0),
              "rest_median": float(np.median(act[:, 5] - act[:, 4]) / 100.0),
              "attn_exit_last": float(us(att[:, 5].max())),
@@ -245,7 +253,8 @@ def phase_report(w, step, ws, G, reps):
         r["critical_wg"]["segments"] = int(crit[6])
         rows.append(r)
     keys = [k for k in rows[0] if k != "critical_wg" and not k.endswith("work_groups")]
-    out = {k: round(float(np.median([r[k] for r in rows])), 2) for k in keys}
+    out = {k: (round(float(np.median([r[k] for r in rows])), 2) if rows[0][k] is not None else None)
+           for k in keys}
     out["active_work_groups"] = rows[0]["active_work_groups"]
     out["combine_work_groups"] = rows[0]["combine_work_groups"]
     mid = sorted(rows, key=lambda r: r["attn_exit_last"])[len(rows) // 2]
@@ -275,6 +284,8 @@ def main():
     ap.add_argument("--cpu-sample-tokens", type=int, default=96,
                     help="block tokens the oracle times (prefill blocks)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-gather-probe", action="store_true",
+                    help="skip the row-gather probe (full-layer decode and verify workloads)")
     ap.add_argument("--eager", action="store_true",
                     help="time K eager calls instead of one replay of K captured steps")
     ap.add_argument("--graph-warmup", type=int, default=400,
@@ -527,6 +538,34 @@ def main():
                     "algorithmic_flops_per_launch": fl,
                     "avg_launch_us": round(attn_avg_ms * 1e3, 2), "avg_launch_us_from": timing_note}
 
+    probe = None
+    if w.L <= 8 and w.layer_kind == 0 and not args.no_gather_probe:
+        # the step's row gather alone (museattn_gather_probe: every visible
+        # key's K and V rows through the table, the attention kernel's
+        # concurrency, no arithmetic), timed like the attention kernel
+        G = P.work_groups(w.B, w.L, w.max_seq_len, w.layer_kind, args.work_groups)
+        chk = torch.empty(G, dtype=torch.int32, device=dev)
+        for _ in range(3):
+            P.gather_probe(d["table"], d["seq_lens"], kp, vp, w.page_size, w.max_seq_len, chk, G)
+        torch.cuda.synchronize()
+        pev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        for e0, e1 in pev:
+            e0.record()
+            P.gather_probe(d["table"], d["seq_lens"], kp, vp, w.page_size, w.max_seq_len, chk, G)
+            e1.record()
+        torch.cuda.synchronize()
+        p_ms = sum(e0.elapsed_time(e1) for e0, e1 in pev) / len(pev)
+        probe = {"kernel": "gather_probe_kernel (the step's K/V rows through the table, "
+                           "no arithmetic)",
+                 "bytes_per_launch": kv, "avg_launch_us": round(p_ms * 1e3, 2),
+                 "gbs": round(kv / (p_ms * 1e-3) / 1e9, 1),
+                 "frac_of_peak": round(kv / (p_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                 "attn_kernel_over_probe": round(attn_avg_ms / p_ms, 4),
+                 "avg_launch_us_from": f"HIP events around each of {args.steps} eager launches"}
+        log(f"gather probe: {probe['avg_launch_us']} us ({probe['gbs']} GB/s); attention kernel "
+            f"/ probe = {probe['attn_kernel_over_probe']}")
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, args.config, args.pool_rows or None, args.cpu_sample,
@@ -553,6 +592,7 @@ def main():
         "cold_cache_graph_replay": cold,
         "oproj": oproj,
         "roofline": roofline,
+        "gather_probe": probe,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

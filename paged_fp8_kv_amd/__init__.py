@@ -35,7 +35,7 @@ STATUS = {
 EXPORTS = ("museattn_abi_version", "museattn_strerror", "museattn_workspace_bytes",
            "museattn_check_args", "museattn_attn_step", "museattn_attn_step_profiled",
            "museattn_work_groups", "museattn_oproj", "museattn_attn_step_oproj",
-           "museattn_attn_step_noalloc")
+           "museattn_attn_step_noalloc", "museattn_gather_probe")
 STATIC_SCRATCH_BYTES = 32 << 20   # MUSEATTN_STATIC_SCRATCH_BYTES
 
 
@@ -90,6 +90,8 @@ def lib() -> ctypes.CDLL:
         L.museattn_attn_step_oproj.argtypes = L.museattn_attn_step.argtypes + [vp, i32, vp, vp, vp]
         L.museattn_attn_step_noalloc.restype = i32
         L.museattn_attn_step_noalloc.argtypes = common + [vp, i32, i32, i32, i32, i64, pp]
+        L.museattn_gather_probe.restype = i32
+        L.museattn_gather_probe.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i64, vp, i32, vp]
         L.museattn_oproj.restype = i32
         L.museattn_oproj.argtypes = [vp, vp, i32, i32, vp, vp]
         _lib = L
@@ -283,3 +285,31 @@ def oproj(a, o_weight, y, stream=None):
     if st != OK:
         raise MuseAttnError(st, "museattn_oproj")
     return y
+
+
+def gather_probe(table, seq_lens, k_cache, v_cache, page_size, max_seq_len, out, work_groups=256,
+                 stream=None):
+    """museattn_gather_probe on torch tensors: reads every visible key's K and
+    V rows of a full-layer step (a memory-system measurement, not the step);
+    out: uint32 device tensor of work_groups checksums (int32 storage)."""
+    import torch
+
+    for name, t in (("table", table), ("seq_lens", seq_lens), ("k_cache", k_cache),
+                    ("v_cache", v_cache), ("out", out)):
+        _need(t.is_cuda and t.is_contiguous(), f"{name} must be a contiguous device tensor")
+    _need(table.dtype == torch.int32 and table.dim() == 2, "table must be int32 [B, stride]")
+    _need(out.numel() >= work_groups and out.element_size() == 4, "out must hold work_groups uint32")
+    if stream is None:
+        stream_ptr = torch.cuda.current_stream(table.device).cuda_stream
+    elif hasattr(stream, "cuda_stream"):
+        stream_ptr = stream.cuda_stream
+    else:
+        stream_ptr = int(stream)
+    st = lib().museattn_gather_probe(table.data_ptr(), seq_lens.data_ptr(), k_cache.data_ptr(),
+                                     v_cache.data_ptr(), int(page_size), int(seq_lens.shape[0]),
+                                     int(table.shape[1]), int(max_seq_len),
+                                     int(k_cache.numel() // ROW_BYTES), out.data_ptr(),
+                                     int(work_groups), stream_ptr)
+    if st != OK:
+        raise MuseAttnError(st, "museattn_gather_probe")
+    return out

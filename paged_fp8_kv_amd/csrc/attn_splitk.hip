@@ -472,9 +472,9 @@ __device__ __forceinline__ void q_values(const StepArgs &a, const QIn &in, const
 #pragma unroll
   for (int k = 0; k < 16; ++k) ss += x[k] * x[k];
   const float ms = head_sum(ss) * (1.0f / 64.0f);
-  const float den = sqrtf(ms + a.eps);
+  const float rden = 1.0f / sqrtf(ms + a.eps);   // q is not rounded to a code: one reciprocal
 #pragma unroll
-  for (int k = 0; k < 16; ++k) y[k] = x[k] / den * wv[k >> 2][k & 3] * a.q_scale;
+  for (int k = 0; k < 16; ++k) y[k] = x[k] * rden * wv[k >> 2][k & 3] * a.q_scale;
   if (a.sliding) {
     const bool low = j < 2;   // dims < 32: x_i c - x_{i+32} s ; else x_{i+32} c + x_i s
 #pragma unroll
@@ -551,17 +551,19 @@ __device__ __forceinline__ void make_q(const StepArgs &a, const QIn &in, const f
 // row(b, p) (task page "Gated attention decode", section "What to compute",
 // the cache line of the listing).  Wave 0/1: k head 0/1, wave 2/3: v head 0/1;
 // lane = dim.  All tokens' inputs are loaded before any is used.
+template <int NT>   // block tokens: 1 (decode) or up to 8 (verify)
 struct RowIn {
-  float x[8];   // the lane's k or v value of each block token
+  float x[NT];   // the lane's k or v value of each block token
   float wk;
 };
 
-__device__ __forceinline__ RowIn load_row_in(const StepArgs &a, int b) {
+template <int NT>
+__device__ __forceinline__ RowIn<NT> load_row_in(const StepArgs &a, int b) {
   const int wave = threadIdx.x >> 6, d = threadIdx.x & 63;
   const int off = (wave < 2 ? K_OFF : V_OFF) + (wave & 1) * D + d;
-  RowIn in;
+  RowIn<NT> in;
 #pragma unroll
-  for (int jt = 0; jt < 8; ++jt) {
+  for (int jt = 0; jt < NT; ++jt) {
     const int t = b * a.L + (jt < a.L ? jt : a.L - 1);
     in.x[jt] = bf16_bits_to_f32(a.qkv[(size_t)t * QKV_W + off]);
   }
@@ -569,18 +571,19 @@ __device__ __forceinline__ RowIn load_row_in(const StepArgs &a, int b) {
   return in;
 }
 
+template <int NT>
 __device__ __forceinline__ void write_new_rows(const StepArgs &a, int b, unsigned own,
-                                               const int (&pos)[8], const float2 (*cs)[32],
-                                               const RowIn &in) {
+                                               const int (&pos)[NT], const float2 (*cs)[32],
+                                               const RowIn<NT> &in) {
   const int wave = threadIdx.x >> 6, d = threadIdx.x & 63;
   const bool is_k = wave < 2;
   const int g = wave & 1;
   const float wk = in.wk;
-  float x[8];
+  float x[NT];
 #pragma unroll
-  for (int jt = 0; jt < 8; ++jt) x[jt] = in.x[jt];
+  for (int jt = 0; jt < NT; ++jt) x[jt] = in.x[jt];
 #pragma unroll
-  for (int jt = 0; jt < 8; ++jt) {
+  for (int jt = 0; jt < NT; ++jt) {
     if (!((own >> jt) & 1u)) continue;   // uniform
     float y = x[jt];
     if (is_k) {
@@ -671,7 +674,8 @@ struct Lds {
 // head in slot `slot`.  The 8 waves take interleaved chunks and both KV heads.
 template <int NBUF>
 __device__ __forceinline__ void process_segment(const StepArgs &a, int b, const KeyRange &r, int x,
-                                                int y, int slot, Lds<0> &sh, bool first) {
+                                                int y, int slot, Lds<0> &sh, bool first,
+                                                bool second) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int n = lane & 15, j = lane >> 4;
   const float qmul = a.kv_scale * (LOG2E / 8.0f);
@@ -682,15 +686,13 @@ __device__ __forceinline__ void process_segment(const StepArgs &a, int b, const 
   // One batch of loads for everything the segment starts with: positions, the
   // first piece's table entries, the tokens' q rows and norm weights, and the
   // inputs of the new k/v rows.
-  int pos[8];
-#pragma unroll
-  for (int jt = 0; jt < 8; ++jt) pos[jt] = a.positions[b * a.L + (jt < a.L ? jt : a.L - 1)];
+  const int pos[1] = {a.positions[b]};   // decode: one block token, token b
   TableIn tin;
-  load_table_in(a, b, r, r.kbase + x * CHUNK, PIECE_CHUNKS, tin);
-  const QIn qin = load_q_in(a, b * a.L, n, j);   // head n of the token
+  load_table_in(a, b, r, r.kbase + x * CHUNK, piece_x(1) - x, tin);
+  const QIn qin = load_q_in(a, b, n, j);   // head n of the token
   const f32x4 *w4 = reinterpret_cast<const f32x4 *>(a.wq + 16 * j);
   const f32x4 wv[4] = {w4[0], w4[1], w4[2], w4[3]};
-  const RowIn rin = load_row_in(a, b);
+  const RowIn<1> rin = load_row_in<1>(a, b);
   __builtin_amdgcn_sched_barrier(0);
   stamp(a, TS_ISSUED, first);
   // the token's RoPE (cos, sin) pairs (L = 1), computed while the loads fly
@@ -721,19 +723,15 @@ __device__ __forceinline__ void process_segment(const StepArgs &a, int b, const 
   // New rows of the block tokens whose key falls in this segment: only this
   // work-group reads them, so a workgroup release before the barrier orders
   // the writes before its own loads.
-  unsigned owned = 0;
-#pragma unroll
-  for (int jt = 0; jt < 8; ++jt) {
-    const int p = pos[jt];
-    const bool in = jt < a.L && p >= r.klo && p <= r.khi &&
-                    (p - r.kbase) / CHUNK >= x && (p - r.kbase) / CHUNK < y;
-    owned |= in ? 1u << jt : 0u;
-  }
-  if (owned && wave < 4) write_new_rows(a, b, owned, pos, sh.cs, rin);
+  const int pn = pos[0];
+  const unsigned owned = pn >= r.klo && pn <= r.khi && (pn - r.kbase) / CHUNK >= x &&
+                         (pn - r.kbase) / CHUNK < y;
+  if (owned && wave < 4) write_new_rows<1>(a, b, owned, pos, sh.cs, rin);
   stamp(a, TS_QREADY, first);
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
   __syncthreads();
   stamp(a, TS_SETUP, first);
+  stamp(a, TS_SEG2_SETUP, second);
 
   for (int pc = 0; pc < npieces; ++pc) {
     const int px = piece_x(pc), py = piece_x(pc + 1);
@@ -742,7 +740,7 @@ __device__ __forceinline__ void process_segment(const StepArgs &a, int b, const 
     if (pc > 0) {
       __syncthreads();   // every wave is done with the previous rows
       TableIn tn;
-      load_table_in(a, b, r, kstart, PIECE_CHUNKS, tn);
+      load_table_in(a, b, r, kstart, nchunks, tn);
       __builtin_amdgcn_sched_barrier(0);
       store_table(a, tn, sh.lrows);
       __syncthreads();
@@ -851,9 +849,9 @@ __device__ __forceinline__ void q_values2(const StepArgs &a, const QIn2 &in, con
 #pragma unroll
   for (int k = 0; k < 16; ++k) ss += x[k] * x[k];
   const float ms = head_sum(ss) * (1.0f / 64.0f);
-  const float den = sqrtf(ms + a.eps);
+  const float rden = 1.0f / sqrtf(ms + a.eps);   // q is not rounded to a code: one reciprocal
 #pragma unroll
-  for (int k = 0; k < 16; ++k) y[k] = x[k] / den * wv[k >> 2][k & 3] * a.q_scale;
+  for (int k = 0; k < 16; ++k) y[k] = x[k] * rden * wv[k >> 2][k & 3] * a.q_scale;
   if (a.sliding) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {   // pair 8j + i: x_i c - x_{i+32} s, x_{i+32} c + x_i s
@@ -875,7 +873,7 @@ __device__ __forceinline__ void q_values2(const StepArgs &a, const QIn2 &in, con
 template <int MODE>
 __device__ __forceinline__ void process_segment_block(const StepArgs &a, int b, int blk,
                                                       const KeyRange &r, int x, int y, int slot,
-                                                      Lds<MODE> &sh, bool first) {
+                                                      Lds<MODE> &sh, bool first, bool second) {
   constexpr bool VERIFY = MODE == 2;
   constexpr int NR = MUSEATTN_BLOCK_PREFETCH;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -923,11 +921,11 @@ __device__ __forceinline__ void process_segment_block(const StepArgs &a, int b, 
   const f32x4 *w4 = reinterpret_cast<const f32x4 *>(a.wq);
   const f32x4 wv[4] = {w4[2 * j], w4[2 * j + 1], w4[8 + 2 * j], w4[8 + 2 * j + 1]};
   int pos[8];
-  RowIn rin;
+  RowIn<8> rin;
   if constexpr (VERIFY) {
 #pragma unroll
     for (int jt = 0; jt < 8; ++jt) pos[jt] = a.positions[b * a.L + (jt < a.L ? jt : a.L - 1)];
-    rin = load_row_in(a, b);
+    rin = load_row_in<8>(a, b);
   }
   __builtin_amdgcn_sched_barrier(0);
 
@@ -1016,12 +1014,13 @@ __device__ __forceinline__ void process_segment_block(const StepArgs &a, int b, 
   if constexpr (VERIFY) {
     // the new rows: a workgroup release before the barrier orders the writes
     // before this work-group's own loads.  (Prefill rows come from rows_kernel.)
-    if (owned && wave < 4) write_new_rows(a, b, owned, pos, sh.cs, rin);
+    if (owned && wave < 4) write_new_rows<8>(a, b, owned, pos, sh.cs, rin);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
   }
   stamp(a, TS_QREADY, first);
   __syncthreads();   // the row ids (and verify's new rows) are in place
   stamp(a, TS_SETUP, first);
+  stamp(a, TS_SEG2_SETUP, second);
 
   for (int pc = 0; pc < npieces; ++pc) {
     const int px = piece_x(pc), py = piece_x(pc + 1);
@@ -1255,10 +1254,11 @@ __global__ __launch_bounds__(THREADS, 2) void attn_kernel(StepArgs a) {
     const KeyRange r = range_from(a, sh.req_len[u], sh.req_p0[u]);
     int b, blk;
     unit_of(a, u, b, blk);
+    stamp(a, TS_SEG2_START, nsegs == 1);
     if constexpr (MODE == 0)
-      process_segment<NBUF>(a, b, r, x, y, w + u, sh, nsegs == 0);
+      process_segment<NBUF>(a, b, r, x, y, w + u, sh, nsegs == 0, nsegs == 1);
     else
-      process_segment_block<MODE>(a, b, blk, r, x, y, w + u, sh, nsegs == 0);
+      process_segment_block<MODE>(a, b, blk, r, x, y, w + u, sh, nsegs == 0, nsegs == 1);
     ++nsegs;
   }
   stamp_count(a, TS_SEGMENTS, (uint64_t)nsegs);

@@ -74,7 +74,9 @@ enum TsSlot {
   TS_SEGMENTS = 6,   // segments processed (a count)
   TS_ISSUED = 7,     // first segment: its batch of loads issued
   TS_TABLE = 8,      // first segment: its row ids stored in LDS (the loads are back)
-  TS_QREADY = 9      // first segment: q operands (and any new rows) done, before the barrier
+  TS_QREADY = 9,     // first segment: q operands (and any new rows) done, before the barrier
+  TS_SEG2_START = 10,   // second segment (if any): entered
+  TS_SEG2_SETUP = 11    // second segment: set-up done (its code is warm by now)
 };
 #ifdef MUSEATTN_PHASE_TIMES
 __device__ __forceinline__ void stamp(const StepArgs &a, int slot, bool on = true) {

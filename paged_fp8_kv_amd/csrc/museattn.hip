@@ -369,6 +369,29 @@ int museattn_attn_step_noalloc(const void *qkv, const int32_t *positions, const 
                       ws, nullptr, nullptr);
 }
 
+int museattn_gather_probe(const int32_t *table, const int32_t *seq_lens, const void *k_cache,
+                          const void *v_cache, int page_size, int B, int table_stride,
+                          int max_seq_len, int64_t num_rows, void *out, int work_groups,
+                          void *stream) {
+  if (!table || !seq_lens || !k_cache || !v_cache || !out) return MUSEATTN_ERR_NULL;
+  if (page_size != 1 && page_size != 64) return MUSEATTN_ERR_PAGE_SIZE;
+  if (B < 1 || B > MAX_BATCH || max_seq_len < 1 || max_seq_len > MAX_SEQ) return MUSEATTN_ERR_SHAPE;
+  if ((int64_t)B * ((max_seq_len + CHUNK - 1) / CHUNK) >= (int64_t(1) << 31)) return MUSEATTN_ERR_SHAPE;
+  if (num_rows < page_size || num_rows % page_size != 0 || num_rows >= (int64_t(1) << 32))
+    return MUSEATTN_ERR_SHAPE;
+  if ((int64_t)table_stride * page_size < max_seq_len || table_stride < 1) return MUSEATTN_ERR_TABLE;
+  if (work_groups < 1 || work_groups > MAX_WORK_GROUPS) return MUSEATTN_ERR_PARAM;
+  if (!aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(table, 4) ||
+      !aligned(seq_lens, 4) || !aligned(out, 4))
+    return MUSEATTN_ERR_ALIGN;
+  (void)hipGetLastError();
+  launch_gather_probe(table, seq_lens, static_cast<const uint8_t *>(k_cache),
+                      static_cast<const uint8_t *>(v_cache), B, table_stride, max_seq_len,
+                      page_size, num_rows, static_cast<uint32_t *>(out), work_groups,
+                      static_cast<hipStream_t>(stream));
+  return hipGetLastError() == hipSuccess ? MUSEATTN_OK : MUSEATTN_ERR_LAUNCH;
+}
+
 namespace {
 // The projection's own arguments (the gated output a is bf16 [T][1024]).
 int check_oproj(const void *a, const void *o_weight, int T, int hidden, const void *y) {

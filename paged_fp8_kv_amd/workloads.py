@@ -317,11 +317,11 @@ class LogicalPool:
     pool[rows] returns [n, 2, 64] bytes; rows that were never placed read as
     the sentinel.  Assigning pool[row] = bytes stores a row."""
 
-    def __init__(self, w: Workload, requests, which: str):
+    def __init__(self, w: Workload, requests, which: str, _values=None):
         ps = w.page_size
         rows, data = [], []
         for b in requests:
-            kb, vb = w.cache_values(b)
+            kb, vb = _values[b] if _values is not None else w.cache_values(b)
             blk = _unit_blocks(w, b, kb if which == "k" else vb)
             r = (np.asarray(w.pages[b], dtype=np.int64)[:, None] * ps + np.arange(ps)[None, :])
             rows.append(r.reshape(-1))
@@ -331,6 +331,14 @@ class LogicalPool:
         order = np.argsort(rows)
         self.rows = rows[order]
         self.data = data[order]
+
+    @staticmethod
+    def pair(w: Workload, requests) -> tuple["LogicalPool", "LogicalPool"]:
+        """The K and V pools of the given requests, each request's cached
+        bytes drawn once for both."""
+        req = list(requests)
+        vals = {b: w.cache_values(b) for b in req}
+        return LogicalPool(w, req, "k", vals), LogicalPool(w, req, "v", vals)
 
     def _find(self, rows):
         rows = np.asarray(rows, dtype=np.int64)

@@ -75,8 +75,7 @@ def oracle_out(w: W.Workload, kb_gpu, vb_gpu, pools=None, tokens=None):
     """Oracle output attending to the GPU's new entries.  pools: host pools
     (numpy) or None for a logical pool of w's requests."""
     if pools is None:
-        kp = W.LogicalPool(w, range(w.B), "k")
-        vp = W.LogicalPool(w, range(w.B), "v")
+        kp, vp = W.LogicalPool.pair(w, range(w.B))
     else:
         kp, vp = pools[0].copy(), pools[1].copy()
     out, _, _ = O.attn_step(w.qkv.float().numpy(), w.positions, w.table, kp, vp, B=w.B, L=w.L,

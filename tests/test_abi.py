@@ -184,3 +184,18 @@ def test_step_oproj_output_must_not_overlap(y_at, status):
         kw["table_stride"], kw["max_seq_len"], kw["num_rows"], ctypes.byref(kw["params"]),
         kw["workspace"], kw["workspace_nbytes"], o_w, 8192, A[y_at] + 4096, None, None)
     assert st == (status if status else -1)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(table=0), -1), (dict(out=0), -1), (dict(ps=16), -2), (dict(B=0), -4),
+    (dict(B=1025), -4), (dict(msl=0), -4), (dict(rows=1 << 32), -4), (dict(stride=999), -5),
+    (dict(wg=0), -8), (dict(wg=65536), -8), (dict(kc=A["kc"] + 8), -6), (dict(out=A["ws"] + 2), -6),
+])
+def test_gather_probe_invalid_arguments_are_rejected(kw, status):
+    """Host-side checks of museattn_gather_probe: they return before any device call."""
+    a = dict(table=A["table"], seq=A["seq"], kc=A["kc"], vc=A["vc"], ps=1, B=4, stride=1000,
+             msl=1000, rows=1 << 20, out=A["ws"], wg=256)
+    a.update(kw)
+    st = P.lib().museattn_gather_probe(a["table"], a["seq"], a["kc"], a["vc"], a["ps"], a["B"],
+                                       a["stride"], a["msl"], a["rows"], a["out"], a["wg"], None)
+    assert st == status

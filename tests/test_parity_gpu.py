@@ -49,20 +49,18 @@ def test_config_parity(cid):
     _untouched_rows_kept(w, d, host)
 
 
-@pytest.mark.parametrize("cid,requests", [("2", [0, 9, 17, 31]), ("4", [0, 5, 15])])
-def test_config_parity_full_size_sampled(cid, requests):
-    """Full-size pools and batch in the launch configuration the bench times;
-    the oracle recomputes a sample of requests (with the shortest and longest
-    contexts among them)."""
+@pytest.mark.parametrize("cid", ["2", "4"])
+def test_config_parity_full_size(cid):
+    """Full-size pools and batch in the launch configuration the bench times
+    (config 2: 32 requests over ~80 GB of pools; config 4: 16 requests, page
+    size 64, kv_scale 1/64): every output element of every request against
+    the oracle, every written byte within 1 ulp."""
     w = W.config(cid)
-    req = sorted(set(requests) | {int(np.argmin(w.ctx)), int(np.argmax(w.ctx))})
-    log(f"[config {cid}] {w.name} B={w.B} pool rows={w.num_rows} checking {req}")
+    log(f"[config {cid}] {w.name} B={w.B} pool rows={w.num_rows} checking all requests")
     d = upload(w)
     run(w, d)
     torch.cuda.synchronize()
-    full_check(w, d, requests=req)
-    # the other requests: finite output, bytes within 1 ulp (checked inside for all)
-    assert torch.isfinite(d["out"].float()).all()
+    full_check(w, d, requests=list(range(w.B)))
     del d
     torch.cuda.empty_cache()
 

@@ -63,11 +63,18 @@ def test_prefill_parity(case):
     _untouched_rows_kept(w, d, host)
 
 
+def _spread(L, n, extra):
+    """n evenly spaced block tokens plus the given ones (group and block edges)."""
+    return sorted({int(x) for x in np.linspace(0, L - 1, n)} | set(extra))
+
+
 SCORED = [
     # name, B, L, ctx, kind, sampled block tokens
-    ("pf-turn1-full-ctx80000-L753", 1, 753, 80000, W.FULL, [0, 1, 15, 16, 377, 751, 752]),
-    ("pf-turn1-sliding-ctx80000-L753", 1, 753, 80000, W.SLIDING, [0, 1, 15, 16, 377, 751, 752]),
-    ("pf-first-turn-sliding-ctx32768-L16384", 1, 16384, 32768, W.SLIDING, [0, 15, 16, 2047, 8191, 16383]),
+    ("pf-turn1-full-ctx80000-L753", 1, 753, 80000, W.FULL, _spread(753, 64, [0, 1, 15, 16, 751, 752])),
+    ("pf-turn1-sliding-ctx80000-L753", 1, 753, 80000, W.SLIDING,
+     _spread(753, 64, [0, 1, 15, 16, 751, 752])),
+    ("pf-first-turn-sliding-ctx32768-L16384", 1, 16384, 32768, W.SLIDING,
+     _spread(16384, 96, [0, 15, 16, 2046, 2047, 2048, 8191, 16383])),
 ]
 
 
@@ -93,7 +100,7 @@ def test_prefill_at_the_unit_limit():
     d = upload(w)
     run(w, d)
     torch.cuda.synchronize()
-    full_check(w, d, tokens=[0, 15, 16, 8191, 16383])
+    full_check(w, d, tokens=_spread(16384, 16, [0, 15, 16, 8191, 16383]))
     assert torch.isfinite(d["out"].float()).all()
     del d
     torch.cuda.empty_cache()
