@@ -553,7 +553,7 @@ __device__ __forceinline__ void make_q(const StepArgs &a, const QIn &in, const f
 // lane = dim.  All tokens' inputs are loaded before any is used.
 template <int NT>   // block tokens: 1 (decode) or up to 8 (verify)
 struct RowIn {
-  float x[NT];   // the lane's k or v value of each block token
+  uint32_t x[NT];   // the lane's k or v value of each block token (bf16 bits)
   float wk;
 };
 
@@ -565,7 +565,7 @@ __device__ __forceinline__ RowIn<NT> load_row_in(const StepArgs &a, int b) {
 #pragma unroll
   for (int jt = 0; jt < NT; ++jt) {
     const int t = b * a.L + (jt < a.L ? jt : a.L - 1);
-    in.x[jt] = bf16_bits_to_f32(a.qkv[(size_t)t * QKV_W + off]);
+    in.x[jt] = a.qkv[(size_t)t * QKV_W + off];
   }
   in.wk = a.wk[d];
   return in;
@@ -581,7 +581,7 @@ __device__ __forceinline__ void write_new_rows(const StepArgs &a, int b, unsigne
   const float wk = in.wk;
   float x[NT];
 #pragma unroll
-  for (int jt = 0; jt < NT; ++jt) x[jt] = in.x[jt];
+  for (int jt = 0; jt < NT; ++jt) x[jt] = bf16_bits_to_f32((uint16_t)in.x[jt]);
 #pragma unroll
   for (int jt = 0; jt < NT; ++jt) {
     if (!((own >> jt) & 1u)) continue;   // uniform
@@ -617,23 +617,22 @@ struct TableIn {
   int32_t unit[MAX_SPLIT_LDS / THREADS];
 };
 
-// Only the first `nchunks` + 2 chunks' entries are loaded (the loops read at
-// most two chunks past a piece's end, for loads that are never used); the
-// rest get page 0, a valid row.
+// Every round is loaded and stored, with indices clamped into the key range
+// (rounds past the piece's chunks repeat its last entry): the loads carry no
+// branch, so the compiler can count them exactly and a later wait for an
+// earlier load need not wait for these.  The table row is a uniform base and
+// the entry a 32-bit offset from it.
 __device__ __forceinline__ void load_table_in(const StepArgs &a, int b, const KeyRange &r,
-                                              int kstart, int nchunks, TableIn &in) {
+                                              int kstart, TableIn &in) {
   const int tid = threadIdx.x;
   const int shift = a.page_size == 1 ? 0 : 6;
   const int32_t *trow = a.table + (int64_t)b * a.table_stride;
-  const int need = (nchunks + 2) * CHUNK;
 #pragma unroll
   for (int it = 0; it < MAX_SPLIT_LDS / THREADS; ++it) {
     const int v = kstart + tid + it * THREADS;
     in.u[it] = v < r.klo ? r.klo : (v > r.khi ? r.khi : v);
+    in.unit[it] = trow[in.u[it] >> shift];
   }
-#pragma unroll
-  for (int it = 0; it < MAX_SPLIT_LDS / THREADS; ++it)
-    in.unit[it] = it * THREADS < need ? trow[in.u[it] >> shift] : 0;
 }
 
 __device__ __forceinline__ void store_table(const StepArgs &a, const TableIn &in, uint32_t *lrows) {
@@ -654,6 +653,7 @@ struct Lds {
   static constexpr int NCS = MODE == 3 ? PREFILL_TB : 8;           // tokens per unit
   uint32_t lrows[MAX_SPLIT_LDS];
   float2 cs[NCS][32];        // RoPE (cos, sin) per token of the unit and pair
+  float rinv[32];            // RoPE inverse frequency per pair (sliding layers)
   union {
     float sm_o[WAVES][HQ][D];   // decode: the 8 waves' O per head
     float mrg[2][64][68];       // verify merge: chunk lane 1's O per KV head and column (padded)
@@ -673,31 +673,36 @@ struct Lds {
 // kbase + 32i ..), processed by the whole work-group, leaving one partial per
 // head in slot `slot`.  The 8 waves take interleaved chunks and both KV heads.
 template <int NBUF>
-__device__ __forceinline__ void process_segment(const StepArgs &a, int b, const KeyRange &r, int x,
-                                                int y, int slot, Lds<0> &sh, bool first,
-                                                bool second) {
+__device__ __forceinline__ void process_segment(const StepArgs &a, int b, const KeyRange &r,
+                                                int p_tok, int x, int y, int slot, Lds<0> &sh,
+                                                bool first, bool second) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int n = lane & 15, j = lane >> 4;
   const float qmul = a.kv_scale * (LOG2E / 8.0f);
   const int nseg = y - x;
   const int npieces = (nseg + PIECE_CHUNKS - 1) / PIECE_CHUNKS;
-  auto piece_x = [&](int pc) { return x + (int)((int64_t)pc * nseg / npieces); };
+  auto piece_x = [&](int pc) { return x + (int)div_floor((int64_t)pc * nseg, npieces); };
 
-  // One batch of loads for everything the segment starts with: positions, the
-  // first piece's table entries, the tokens' q rows and norm weights, and the
-  // inputs of the new k/v rows.
-  const int pos[1] = {a.positions[b]};   // decode: one block token, token b
+  // One batch of loads for everything the segment starts with: the first
+  // piece's table entries, the token's q row and norm weights and the inputs
+  // of its new k/v row (kept as raw bits: converting them here would wait for
+  // the loads).  The token's position came with the plan (p_tok).
+  const int px1 = piece_x(1);
   TableIn tin;
-  load_table_in(a, b, r, r.kbase + x * CHUNK, piece_x(1) - x, tin);
+  load_table_in(a, b, r, r.kbase + x * CHUNK, tin);
+  // every wave loads q (wave 0 builds the Q^T operands) and the new row's
+  // inputs (waves 0-3 write it): no branch around the loads
   const QIn qin = load_q_in(a, b, n, j);   // head n of the token
   const f32x4 *w4 = reinterpret_cast<const f32x4 *>(a.wq + 16 * j);
   const f32x4 wv[4] = {w4[0], w4[1], w4[2], w4[3]};
-  const RowIn<1> rin = load_row_in<1>(a, b);
+  const RowIn<1> rin = load_row_in<1>(a, b);   // every wave: no branch around the loads
+  int pt = p_tok < 0 ? 0 : (p_tok > a.max_seq_len - 1 ? a.max_seq_len - 1 : p_tok);
+  const int pos[1] = {pt};   // decode: one block token, token b
   __builtin_amdgcn_sched_barrier(0);
   stamp(a, TS_ISSUED, first);
   // the token's RoPE (cos, sin) pairs (L = 1), computed while the loads fly
   float2 csv = make_float2(1.0f, 0.0f);
-  if (a.sliding && tid < 32) csv = rope_cs(pos[0], tid);
+  if (a.sliding && tid < 32) csv = rope_cs_inv(pos[0], sh.rinv[tid]);
 
   __syncthreads();   // the previous segment is done with sh.cs, sh.lrows and the merge buffers
   if (a.sliding) {
@@ -740,7 +745,7 @@ __device__ __forceinline__ void process_segment(const StepArgs &a, int b, const 
     if (pc > 0) {
       __syncthreads();   // every wave is done with the previous rows
       TableIn tn;
-      load_table_in(a, b, r, kstart, nchunks, tn);
+      load_table_in(a, b, r, kstart, tn);
       __builtin_amdgcn_sched_barrier(0);
       store_table(a, tn, sh.lrows);
       __syncthreads();
@@ -881,7 +886,7 @@ __device__ __forceinline__ void process_segment_block(const StepArgs &a, int b, 
   const float qmul = a.kv_scale * (LOG2E / 8.0f);
   const int nseg = y - x;
   const int npieces = (nseg + PIECE_CHUNKS - 1) / PIECE_CHUNKS;
-  auto piece_x = [&](int pc) { return x + (int)((int64_t)pc * nseg / npieces); };
+  auto piece_x = [&](int pc) { return x + (int)div_floor((int64_t)pc * nseg, npieces); };
   const int g = wave & 1;
   const int cq = VERIFY ? (wave >> 1) & 1 : wave >> 1;   // column tiles 2cq, 2cq + 1
   const int cl = VERIFY ? wave >> 2 : 0;                 // verify: the wave's sub-chunk
@@ -900,7 +905,7 @@ __device__ __forceinline__ void process_segment_block(const StepArgs &a, int b, 
   const int cs_tk = tid >> 5;   // sliding: this thread's RoPE pair is (token cs_tk, pair tid % 32)
   const int cs_p = a.sliding ? a.positions[b * a.L + j0 + (cs_tk < nt ? cs_tk : nt - 1)] : 0;
   TableIn tin;
-  load_table_in(a, b, r, r.kbase + x * CHUNK, piece_x(1) - x, tin);
+  load_table_in(a, b, r, r.kbase + x * CHUNK, tin);
   int eu[NR], eunit[NR];
 #pragma unroll
   for (int k = 0; k < NR; ++k) {
@@ -961,7 +966,7 @@ __device__ __forceinline__ void process_segment_block(const StepArgs &a, int b, 
   // RoPE (cos, sin) of the unit's tokens (512 threads: up to 16 tokens x 32
   // pairs), computed while the loads fly
   float2 csv = make_float2(1.0f, 0.0f);
-  if (a.sliding && cs_tk < nt) csv = rope_cs(cs_p, tid & 31);
+  if (a.sliding && cs_tk < nt) csv = rope_cs_inv(cs_p, sh.rinv[tid & 31]);
 
   __syncthreads();   // the previous segment is done with sh.cs, sh.lrows and the stage buffers
   if (a.sliding) {
@@ -1029,7 +1034,7 @@ __device__ __forceinline__ void process_segment_block(const StepArgs &a, int b, 
     if (pc > 0) {
       __syncthreads();   // every wave is done with the previous rows
       TableIn tn;
-      load_table_in(a, b, r, kstart, py - px, tn);
+      load_table_in(a, b, r, kstart, tn);
       __builtin_amdgcn_sched_barrier(0);
       store_table(a, tn, sh.lrows);
       __syncthreads();
@@ -1172,9 +1177,12 @@ __global__ __launch_bounds__(THREADS, 2) void attn_kernel(StepArgs a) {
       int ub;
       unit_of(a, u, ub, ublk[k]);
       sl[k] = a.seq_lens[ub];
-      p0[k] = a.sliding ? a.positions[ub * a.L + ublk[k] * a.tb] : 0;
+      p0[k] = a.positions[ub * a.L + ublk[k] * a.tb];   // (decode reads its token's here)
     }
     __builtin_amdgcn_sched_barrier(0);
+    // the RoPE frequencies (kernel arguments), read while the lengths are in
+    // flight; the segments take them from LDS, with no load of their own
+    if (a.sliding && tid < 32) sh.rinv[tid] = rope_inv(tid);
 #pragma unroll
     for (int k = 0; k < RPT; ++k) {
       const int len = unit_len(a, sl[k], ublk[k]);
@@ -1233,7 +1241,7 @@ __global__ __launch_bounds__(THREADS, 2) void attn_kernel(StepArgs a) {
     stamp(a, TS_EXIT);
     return;
   }
-  const int64_t cb = (int64_t)w * Ct / G, ce = (int64_t)(w + 1) * Ct / G;
+  const int64_t cb = div_floor((int64_t)w * Ct, G), ce = div_floor((int64_t)(w + 1) * Ct, G);
   auto cost_of = [&](int uu) { return (int64_t)sh.pref[uu] + (int64_t)uu * per; };
   int u = 0;
   {
@@ -1256,7 +1264,7 @@ __global__ __launch_bounds__(THREADS, 2) void attn_kernel(StepArgs a) {
     unit_of(a, u, b, blk);
     stamp(a, TS_SEG2_START, nsegs == 1);
     if constexpr (MODE == 0)
-      process_segment<NBUF>(a, b, r, x, y, w + u, sh, nsegs == 0, nsegs == 1);
+      process_segment<NBUF>(a, b, r, sh.req_p0[u], x, y, w + u, sh, nsegs == 0, nsegs == 1);
     else
       process_segment_block<MODE>(a, b, blk, r, x, y, w + u, sh, nsegs == 0, nsegs == 1);
     ++nsegs;

@@ -124,11 +124,11 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
 // key range).  Page (or row) ids are clamped into the pool so that no table
 // value can address memory outside it.
 __device__ __forceinline__ uint32_t cache_row(const StepArgs &a, int b, int u) {
-  const int ps = a.page_size;
-  const uint32_t units = (uint32_t)(a.num_rows / ps);
-  uint32_t unit = (uint32_t)a.table[(int64_t)b * a.table_stride + u / ps];
+  const int shift = a.page_size == 1 ? 0 : 6;   // page size 1 or 64
+  const uint32_t units = (uint32_t)(a.num_rows >> shift);
+  uint32_t unit = (uint32_t)a.table[(int64_t)b * a.table_stride + (u >> shift)];
   unit = unit < units ? unit : units - 1;
-  return unit * (uint32_t)ps + (uint32_t)(u % ps);
+  return (unit << shift) + (uint32_t)(u & (a.page_size - 1));
 }
 
 // The union key range of request b's block tokens.  khi = seq_len - 1; klo =
@@ -177,11 +177,28 @@ __device__ __forceinline__ float wave_sum(float x) {
   return __int_as_float(q[0]) + __int_as_float(q[1]);
 }
 
+// floor(n / d) for 0 <= n < 2^50 and 0 < d < 2^31.  gfx950 has no 64-bit
+// integer divide: the compiler's sequence is ~130 scalar instructions, which
+// every wave of a work-group runs on the CU's one scalar unit.  Here n times
+// the double reciprocal of d (v_rcp_f64, a few ulp: within two of the true
+// quotient for such operands) is corrected to the exact floor with integer
+// products.
+__device__ __forceinline__ int64_t div_floor(int64_t n, int64_t d) {
+  int64_t q = (int64_t)((double)n * __builtin_amdgcn_rcp((double)d));
+  // at most two steps either way; straight-line selects, no loop (a loop's
+  // block boundaries would keep the scheduler from moving loads across it)
+  q -= q * d > n ? 1 : 0;
+  q -= q * d > n ? 1 : 0;
+  q += (q + 1) * d <= n ? 1 : 0;
+  q += (q + 1) * d <= n ? 1 : 0;
+  return q;
+}
+
 // Cost unit c of C spread over G work-groups (work-group w owns units
 // [floor(w C / G), floor((w + 1) C / G))) belongs to work-group
 // floor(((c + 1) G - 1) / C).
 __device__ __forceinline__ int wg_of_chunk(int64_t c, int64_t C, int G) {
-  return (int)(((c + 1) * G - 1) / C);
+  return (int)div_floor((c + 1) * G - 1, C);
 }
 
 // Sum over each 16-lane row (DPP only).
@@ -221,17 +238,24 @@ __device__ __forceinline__ uint8_t to_e4m3(float x) {
 // the host fills once per call); sin/cos of that fp32 angle are taken in
 // double so large positions keep full accuracy (task page "Gated attention
 // decode", section "What to compute", the rope line; sliding layers only,
-// section "Shapes").  The table is read from the kernel's argument block,
-// whose first member is the StepArgs (a per-lane index into the by-value
-// argument itself would make the compiler copy it to scratch).
-__device__ __forceinline__ float2 rope_cs(int p, int i) {
+// section "Shapes").
+//
+// The table is read from the kernel's argument block, whose first member is
+// the StepArgs (a per-lane index into the by-value argument itself would make
+// the compiler copy it to scratch).
+__device__ __forceinline__ float rope_inv(int i) {
   const char *args = (const char *)__builtin_amdgcn_kernarg_segment_ptr();
-  const float *rope_inv = reinterpret_cast<const float *>(args + offsetof(StepArgs, rope_inv));
-  const float inv = rope_inv[i];
+  return reinterpret_cast<const float *>(args + offsetof(StepArgs, rope_inv))[i];
+}
+
+// (cos, sin) of position p for a pair whose inverse frequency is inv.
+__device__ __forceinline__ float2 rope_cs_inv(int p, float inv) {
   const float th = (float)p * inv;
   double sd, cd;
   sincos((double)th, &sd, &cd);
   return make_float2((float)cd, (float)sd);
 }
+
+__device__ __forceinline__ float2 rope_cs(int p, int i) { return rope_cs_inv(p, rope_inv(i)); }
 
 }  // namespace museattn

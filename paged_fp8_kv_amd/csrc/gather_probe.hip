@@ -102,7 +102,8 @@ __global__ __launch_bounds__(THREADS) void gather_probe_kernel(
 
   const int64_t C = pref[B];
   const int G = gridDim.x;
-  const int64_t cb = (int64_t)blockIdx.x * C / G, ce = (int64_t)(blockIdx.x + 1) * C / G;
+  const int64_t cb = div_floor((int64_t)blockIdx.x * C, G);
+  const int64_t ce = div_floor((int64_t)(blockIdx.x + 1) * C, G);
   uint32_t acc = 0;
   int b = 0;
   while (b < B - 1 && pref[b + 1] <= cb) ++b;
