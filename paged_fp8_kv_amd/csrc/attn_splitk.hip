@@ -896,16 +896,20 @@ __device__ __forceinline__ void process_segment_block(const StepArgs &a, int b, 
   nc = nc < 0 ? 0 : (nc > 2 ? 2 : nc);
   auto tok = [&](int c) { return 4 * cq + 2 * c + (n >> 3); };   // unit token of the lane column
 
-  // One batch of loads: the first piece's table entries (also, separately,
-  // those of the rows this thread stages in the first BLOCK_PREFETCH steps),
-  // the column tokens' positions and q, the q norm weights and (verify) the
-  // new rows' inputs.
+  // One batch of loads.  First what the first steps' stage loads depend on:
+  // (verify) the block tokens' positions, lane j holding token j % 8's (a
+  // per-lane value: kept in a vector register, it is not waited for until
+  // used), and the table entries of the rows this thread stages in the first
+  // BLOCK_PREFETCH steps.  Then the first piece's table entries, the column
+  // tokens' positions and q, the RoPE position of this thread's pair, the q
+  // norm weights and (verify) the new rows' inputs.  No load sits behind a
+  // branch, so the compiler counts them exactly: a wait for the first ones is
+  // not a wait for the batch.
   const int shift = a.page_size == 1 ? 0 : 6;
   const int nsteps0 = (piece_x(1) - x + 1) >> 1;
   const int cs_tk = tid >> 5;   // sliding: this thread's RoPE pair is (token cs_tk, pair tid % 32)
-  const int cs_p = a.sliding ? a.positions[b * a.L + j0 + (cs_tk < nt ? cs_tk : nt - 1)] : 0;
-  TableIn tin;
-  load_table_in(a, b, r, r.kbase + x * CHUNK, tin);
+  int posv = 0;
+  if constexpr (VERIFY) posv = a.positions[b * a.L + ((lane & 7) < a.L ? (lane & 7) : a.L - 1)];
   int eu[NR], eunit[NR];
 #pragma unroll
   for (int k = 0; k < NR; ++k) {
@@ -914,6 +918,8 @@ __device__ __forceinline__ void process_segment_block(const StepArgs &a, int b, 
     eu[k] = v < r.klo ? r.klo : (v > r.khi ? r.khi : v);
     eunit[k] = a.table[(int64_t)b * a.table_stride + (eu[k] >> shift)];
   }
+  TableIn tin;
+  load_table_in(a, b, r, r.kbase + x * CHUNK, tin);
   int cpos[2];
   QIn2 qin[2];
 #pragma unroll
@@ -923,28 +929,24 @@ __device__ __forceinline__ void process_segment_block(const StepArgs &a, int b, 
     cpos[c] = a.positions[t];
     qin[c] = load_q_in2(a, t, 8 * g + (n & 7), j);
   }
+  const int cs_p = a.positions[b * a.L + j0 + (cs_tk < nt ? cs_tk : nt - 1)];
   const f32x4 *w4 = reinterpret_cast<const f32x4 *>(a.wq);
   const f32x4 wv[4] = {w4[2 * j], w4[2 * j + 1], w4[8 + 2 * j], w4[8 + 2 * j + 1]};
-  int pos[8];
   RowIn<8> rin;
-  if constexpr (VERIFY) {
-#pragma unroll
-    for (int jt = 0; jt < 8; ++jt) pos[jt] = a.positions[b * a.L + (jt < a.L ? jt : a.L - 1)];
-    rin = load_row_in<8>(a, b);
-  }
+  if constexpr (VERIFY) rin = load_row_in<8>(a, b);
   __builtin_amdgcn_sched_barrier(0);
 
   // Verify: the block tokens whose new rows fall in this segment (only this
-  // work-group reads them; they are written below).
+  // work-group reads them; they are written below): lane j < 8 tests token j.
   unsigned owned = 0;
+  int pos[8];
   if constexpr (VERIFY) {
+    const int jt = lane & 7;
+    const bool in = lane < 8 && jt < a.L && posv >= r.klo && posv <= r.khi &&
+                    (posv - r.kbase) / CHUNK >= x && (posv - r.kbase) / CHUNK < y;
+    owned = (unsigned)__ballot(in);
 #pragma unroll
-    for (int jt = 0; jt < 8; ++jt) {
-      const int p = pos[jt];
-      const bool in = jt < a.L && p >= r.klo && p <= r.khi &&
-                      (p - r.kbase) / CHUNK >= x && (p - r.kbase) / CHUNK < y;
-      owned |= in ? 1u << jt : 0u;
-    }
+    for (int t2 = 0; t2 < 8; ++t2) pos[t2] = __builtin_amdgcn_readlane(posv, t2);
   }
   // The first steps' stage loads leave now, from the thread's own table
   // entries, so they overlap the set-up below -- unless the segment holds new
