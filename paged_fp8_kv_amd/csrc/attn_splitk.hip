@@ -37,6 +37,11 @@
 namespace museattn {
 
 constexpr float LOG2E = 1.4426950408889634f;
+
+template <class T>
+__device__ __forceinline__ void part_store(T *p, T v) {
+  *p = v;
+}
 constexpr int MAX_SPLIT_LDS = 4096;   // table entries cached per work-group
 // log2 units a stale reference max may lag: P <= 2^15 stays inside fp16's
 // range (65504) in the block products
@@ -819,10 +824,9 @@ __device__ __forceinline__ void process_segment(const StepArgs &a, int b, const 
     }
   }
   const size_t e = (size_t)slot * HQ + h;   // L = 1
-  *reinterpret_cast<f32x2 *>(a.part_o + e * D + d2) = o;
+  part_store(reinterpret_cast<f32x2 *>(a.part_o + e * D + d2), o);
   if ((tid & 31) == 0) {
-    a.part_ml[e * 2] = M;
-    a.part_ml[e * 2 + 1] = lt;
+    part_store(reinterpret_cast<f32x2 *>(a.part_ml + e * 2), f32x2{M, lt});
   }
   stamp(a, TS_PARTIAL, first);
 }
@@ -1138,12 +1142,11 @@ __device__ __forceinline__ void process_segment_block(const StepArgs &a, int b, 
       if (tk >= nt) continue;
       const size_t e = ((size_t)slot * a.tb + tk) * HQ + 8 * g + (n & 7);
       if (j == 0) {
-        a.part_ml[e * 2] = st.m[c];
-        a.part_ml[e * 2 + 1] = lsum[c];
+        part_store(reinterpret_cast<f32x2 *>(a.part_ml + e * 2), f32x2{st.m[c], lsum[c]});
       }
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
-        *reinterpret_cast<f32x4 *>(a.part_o + e * D + 16 * dt + 4 * j) = st.o[dt][c];
+        part_store(reinterpret_cast<f32x4 *>(a.part_o + e * D + 16 * dt + 4 * j), st.o[dt][c]);
     }
   }
   stamp(a, TS_PARTIAL, first);
