@@ -224,10 +224,11 @@ __device__ __forceinline__ void compute_chunk(const RowBuf &rb, int u0, int lane
 // tokens 2ct and 2ct + 1 of the unit (lane column n: token 2ct + n/8, head
 // 8g + n%8).  The work-group moves through a segment in steps of 64 keys (two
 // 32-key sub-chunks) that its 8 waves share:
-//  * staging: thread t loads 32 B of key t/8's K row (t%8 < 4) or V row
-//    (t%8 >= 4), so 4 lanes read one whole 128-B row; the bytes are converted
-//    to fp16 (exactly) once for the work-group and written, key-major, into
-//    one of two LDS stage buffers (rows padded against bank conflicts).  The
+//  * staging: lanes 0-31 of each wave load 32 B of a K row, lanes 32-63 32 B
+//    of a V row (stage_map), so 4 lanes read one whole 128-B row; the bytes
+//    are converted to fp16 (exactly) once for the work-group and written,
+//    key-major, into one of two LDS stage buffers (K chunks swizzled, V rows
+//    padded, so that no LDS pass meets a bank twice).  The
 //    loads run BLOCK_PREFETCH steps ahead in registers; one barrier per step.
 //  * S^T (32 keys x 16 columns) per sub-chunk and column tile: 2 key tiles x
 //    2 K-steps of v_mfma_f32_16x16x32_f16; A = K rows from LDS (K-step kk:
@@ -246,8 +247,21 @@ __device__ __forceinline__ void compute_chunk(const RowBuf &rb, int u0, int lane
 // column tiles per KV head): wave w takes KV head w % 2, column tiles 2(w/2)
 // and 2(w/2) + 1, and both sub-chunks of each step.
 constexpr int STAGE_KEYS = 64;
-constexpr int KROW = 272;   // LDS bytes per key of the K stage: 2 heads x 64 fp16, + 16
-constexpr int VROW = 288;   // of the V stage: + 32 (a transposing read spans 4 rows x 32 B)
+// LDS passes on gfx950 (measured with the bank-conflict counter, one pair of
+// active lanes at a time): ds_read_b128 serves 16 lanes per pass, lanes
+// {0-3, 12-15, 20-23, 24-27}, {4-7, 8-11, 16-19, 28-31} and the same sets + 32,
+// over 64 banks of 4 B; ds_write_b128 serves 8 consecutive lanes per pass over
+// 32 banks.  A read pass is conflict-free when its 16 lanes hit 16 distinct
+// 16-B bank quads (address / 16 mod 16), a write pass when its 8 lanes hit
+// distinct quads mod 8.
+// K stage: 256-B rows (2 heads x 64 fp16), 16-B chunk c of key r at slot
+// c ^ (r % 16).  The operand reads (keys n = 0..15 of a tile, chunk cb + j
+// with cb a multiple of 4) then hit quads cb ^ j ^ n, distinct in every read
+// pass; the stores (keys r..r+7, one chunk) hit quads c ^ (r % 8) mod 8.  A
+// plain padded stride meets only one of the two (272 B: the reads conflict;
+// 288 B: the stores do).
+constexpr int KROW = 256;   // LDS bytes per key of the K stage
+constexpr int VROW = 288;   // of the V stage: + 32 B (see stage_map for its chunk order)
 
 struct Stage {
   uint8_t k[STAGE_KEYS * KROW];
@@ -327,19 +341,23 @@ __device__ __forceinline__ int v_slot(int part, int q) { return (q - (part & 1))
 
 __device__ __forceinline__ void stage_store(const StageIn &in, Stage &st) {
   const StageMap m = stage_map(threadIdx.x);
-  uint8_t *dst = m.v ? st.v + m.key * VROW + m.part * 64 : st.k + m.key * KROW + m.part * 64;
   const f16x8 c[4] = {fp8x8_to_f16(in.x[0].x, in.x[0].y), fp8x8_to_f16(in.x[0].z, in.x[0].w),
                       fp8x8_to_f16(in.x[1].x, in.x[1].y), fp8x8_to_f16(in.x[1].z, in.x[1].w)};
+  // per-lane offsets (no branch: K and V lanes share each store instruction)
+  uint8_t *dst = m.v ? st.v + m.key * VROW + m.part * 64 : st.k + m.key * KROW;
 #pragma unroll
-  for (int q = 0; q < 4; ++q)
-    *reinterpret_cast<f16x8 *>(dst + 16 * (m.v ? v_slot(m.part, q) : q)) = c[q];
+  for (int q = 0; q < 4; ++q) {
+    const int slot = m.v ? v_slot(m.part, q) : (4 * m.part + q) ^ (m.key & 15);
+    *reinterpret_cast<f16x8 *>(dst + 16 * slot) = c[q];
+  }
 }
 
 // A operand of S^T: key tile t of sub-chunk sc, K-step kk, KV head g.
 __device__ __forceinline__ f16x8 k_operand(const Stage &st, int sc, int t, int kk, int n, int j,
                                            int g) {
-  return *reinterpret_cast<const f16x8 *>(st.k + (32 * sc + 16 * t + n) * KROW + g * 128 +
-                                           kk * 64 + j * 16);
+  // chunk 8g + 4kk + j of key 32sc + 16t + n, at slot (8g + 4kk) ^ j ^ n
+  return *reinterpret_cast<const f16x8 *>(st.k + (32 * sc + 16 * t + n) * KROW +
+                                           16 * ((8 * g + 4 * kk) ^ j ^ n));
 }
 
 // A operand of O^T = V^T . P^T: dim tile dt of sub-chunk sc, KV head g.  Lane
