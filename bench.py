@@ -244,7 +244,16 @@ def phase_report(w, step, ws, G, reps):
                                                      if len(two) else None),
              "partial_median": float(np.median(act[:, 4] - act[:, 3]) / 100.0),
              "rest_median": float(np.median(act[:, 5] - act[:, 4]) / 100.0),
+             "setup_done_p50": float(np.median(us(act[:, 2]))),
+             "setup_done_max": float(us(act[:, 2].max())),
+             "attn_exit_p10": float(np.percentile(us(act[:, 5]), 10)),
+             "attn_exit_p50": float(np.median(us(act[:, 5]))),
+             "attn_exit_p90": float(np.percentile(us(act[:, 5]), 90)),
              "attn_exit_last": float(us(att[:, 5].max())),
+             # work-group w runs on XCD w % 8 (round-robin dispatch)
+             "attn_exit_by_xcd_median": [float(np.median(us(g[g[:, 6] > 0, 5])))
+                                         if (g[:, 6] > 0).any() else 0.0
+                                         for g in (att[x::8] for x in range(8))],
              "combine_entry_first": float(us(comb[:, 0].min())),
              "combine_exit_last": float(us(comb[:, 1].max())),
              "active_work_groups": int(len(act)), "combine_work_groups": int(len(comb))}
@@ -253,8 +262,10 @@ def phase_report(w, step, ws, G, reps):
         r["critical_wg"]["segments"] = int(crit[6])
         rows.append(r)
     keys = [k for k in rows[0] if k != "critical_wg" and not k.endswith("work_groups")]
-    out = {k: (round(float(np.median([r[k] for r in rows])), 2) if rows[0][k] is not None else None)
-           for k in keys}
+    med = lambda k: (round(float(np.median([r[k] for r in rows])), 2)  # noqa: E731
+                     if not isinstance(rows[0][k], list) else
+                     [round(float(x), 2) for x in np.median([r[k] for r in rows], axis=0)])
+    out = {k: (med(k) if rows[0][k] is not None else None) for k in keys}
     out["active_work_groups"] = rows[0]["active_work_groups"]
     out["combine_work_groups"] = rows[0]["combine_work_groups"]
     mid = sorted(rows, key=lambda r: r["attn_exit_last"])[len(rows) // 2]
@@ -301,8 +312,8 @@ def main():
                          "phase breakdown of the step instead of the benchmark line")
     args = ap.parse_args()
     if args.phases:   # before the package is imported: it reads MUSEATTN_LIB once
-        os.environ["MUSEATTN_LIB"] = os.path.join(ROOT, "paged_fp8_kv_amd",
-                                                  "libmuseattn_phases.so")
+        os.environ.setdefault("MUSEATTN_LIB", os.path.join(ROOT, "paged_fp8_kv_amd",
+                                                           "libmuseattn_phases.so"))
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the step "

@@ -245,13 +245,14 @@ int museattn_attn_step_oproj(const void *qkv, const int32_t *positions, const in
 
 /* A memory-system probe, not part of the step: reads the K and V rows of
  * every key position 0 .. seq_lens[b] - 1 of every request (the keys a
- * full-layer decode step attends to) through the table, with the attention
- * kernel's concurrency (work_groups work-groups of 8 waves, equal shares of
- * all requests' 32-key chunks, two chunks of rows in flight per wave), and
- * writes one checksum of the bytes per work-group to out (uint32
- * [work_groups], device).  Its duration is the time the step's row gather
- * takes on its own: the ceiling of the attention kernel on this workload.
- * Arguments as in museattn_attn_step; 1 <= work_groups <= 65535.  Statuses:
+ * full-layer decode step attends to) through the table, each key once, with
+ * nothing else to do: work_groups work-groups of 8 waves take equal shares of
+ * all requests' keys laid end to end, stage their row ids in LDS and stream
+ * the rows with 128-byte-row loads.  It writes one XOR checksum of the rows'
+ * 32-bit words per work-group to out (uint32 [work_groups], device).  Its
+ * duration is the time this part needs to gather the step's rows: the
+ * ceiling of the attention kernel on this workload.  Arguments as in
+ * museattn_attn_step; 1 <= work_groups <= 65535.  Statuses:
  * MUSEATTN_ERR_NULL, _PAGE_SIZE, _SHAPE, _TABLE, _PARAM, _ALIGN, _LAUNCH. */
 int museattn_gather_probe(const int32_t *table, const int32_t *seq_lens, const void *k_cache,
                           const void *v_cache, int page_size, int B, int table_stride,

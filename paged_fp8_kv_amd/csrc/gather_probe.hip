@@ -1,13 +1,19 @@
-// A memory-system probe, not part of the step: the read rate of the step's
-// own K/V row gather.  It reads every visible key's K and V rows of a
-// full-layer decode step (positions 0 .. seq_lens[b] - 1 of each request,
-// through the page table) with the attention kernel's decode loads and
-// concurrency -- 256 work-groups of 8 waves, each taking an equal share of
-// all requests' 32-key chunks, the row ids of up to 4096 keys staged in LDS,
-// the same load instructions per chunk, two chunks in flight per wave -- and
-// folds the bytes into one checksum per work-group, so no load can be
-// dropped.  Its time is the ceiling the attention kernel would reach if its
-// arithmetic were free.
+// A memory-system probe, not part of the step: how fast this part can read
+// the step's K/V rows with nothing else to do.  It reads both rows of every
+// visible key of a full-layer decode step (positions 0 .. seq_lens[b] - 1 of
+// each request, through the page table) exactly once and folds their 32-bit
+// words into one XOR checksum per work-group, so no load can be dropped.
+//
+// It is built as the fastest plain gather found on this part, not as a copy
+// of the attention kernel's loads, so that its time is the ceiling for the
+// step's gather: work-group w takes keys [w K / G, (w + 1) K / G) of the K
+// keys of all requests laid end to end; it stages the row ids of up to 12,288
+// of them in LDS (all table loads issued before the first store: one round
+// trip); each wave then walks its own contiguous share in groups of 16 keys,
+// lane l reading bytes 16 (l % 8) .. + 15 of the K and V rows of key l / 8 of
+// a batch of 8 (8 lanes cover a 128-byte row), with two groups (8 KB per
+// wave) in flight.  Deeper rings, 16-wave or two-per-CU work-groups and
+// direct-to-LDS loads measured the same.
 #include "device_common.h"
 #include "launch.h"
 
@@ -15,130 +21,139 @@ namespace museattn {
 
 namespace {
 
-constexpr int PROBE_ROWS_LDS = 4096;   // row ids staged per piece
+constexpr int PROBE_IDS = 12288;              // row ids staged per piece (48 KB)
+constexpr int PROBE_PER_THREAD = PROBE_IDS / THREADS;
+constexpr int PROBE_BATCHES = 2;              // batches of 8 keys per group
+constexpr int PROBE_KPG = 8 * PROBE_BATCHES;  // keys per group
+constexpr int PROBE_RING = 2;                 // groups in flight per wave
 
-struct ProbeRows {
-  uint4 k[4];   // 16-byte pieces of the K rows of keys n and 16 + n
-  uint2 v[8];   // 8-byte pieces of the V rows of the 8 keys 4j.. and 16 + 4j..
+struct ProbeGroup {
+  uint4 k[PROBE_BATCHES], v[PROBE_BATCHES];
 };
-
-// The attention kernel's own decode loads of one 32-key chunk (8 KB): lane
-// (n = lane%16, j = lane/16) reads bytes 16j .. and 64 + 16j .. of the K rows
-// of keys n and 16 + n, and bytes 8n .. 8n + 7 of the V rows of keys 4j ..
-// 4j + 3 and 16 + 4j .. 16 + 4j + 3 (one V load instruction covers 4 whole
-// rows).
-__device__ __forceinline__ void probe_load(ProbeRows &r, const uint8_t *__restrict__ kc,
-                                           const uint8_t *__restrict__ vc, const uint32_t *rows,
-                                           int n, int j) {
-  const uint64_t r0 = rows[n], r1 = rows[16 + n];
-  const uint8_t *k0 = kc + r0 * ROW + 16 * j, *k1 = kc + r1 * ROW + 16 * j;
-  r.k[0] = *reinterpret_cast<const uint4 *>(k0);
-  r.k[1] = *reinterpret_cast<const uint4 *>(k0 + 64);
-  r.k[2] = *reinterpret_cast<const uint4 *>(k1);
-  r.k[3] = *reinterpret_cast<const uint4 *>(k1 + 64);
-  const uint4 va = *reinterpret_cast<const uint4 *>(rows + 4 * j);
-  const uint4 vb = *reinterpret_cast<const uint4 *>(rows + 16 + 4 * j);
-  const uint32_t vr[8] = {va.x, va.y, va.z, va.w, vb.x, vb.y, vb.z, vb.w};
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-    r.v[i] = *reinterpret_cast<const uint2 *>(vc + (uint64_t)vr[i] * ROW + 8 * n);
-}
-
-__device__ __forceinline__ uint32_t probe_fold(const ProbeRows &r) {
-  uint32_t x = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) x ^= r.k[i].x ^ r.k[i].y ^ r.k[i].z ^ r.k[i].w;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) x ^= r.v[i].x ^ r.v[i].y;
-  return x;
-}
 
 __global__ __launch_bounds__(THREADS) void gather_probe_kernel(
     const int32_t *__restrict__ table, const int32_t *__restrict__ seq_lens,
     const uint8_t *__restrict__ kc, const uint8_t *__restrict__ vc, int B, int table_stride,
     int max_seq_len, int page_size, int64_t num_rows, uint32_t *__restrict__ out) {
-  __shared__ int pref[MAX_BATCH + 1];
-  __shared__ int scan[WAVES];
-  __shared__ uint32_t rows[PROBE_ROWS_LDS];
+  __shared__ int64_t pref[MAX_BATCH + 1];
+  __shared__ int64_t scan[WAVES];
+  __shared__ uint32_t sid[PROBE_IDS];
   __shared__ uint32_t red[WAVES];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int n = lane & 15, j = lane >> 4;
   const int shift = page_size == 1 ? 0 : 6;
   const uint32_t units = (uint32_t)(num_rows >> shift);
 
-  // chunk counts of the requests (two per thread) and their prefix sums
-  int cnt[2], sl[2], sum = 0;
+  // key counts of the requests (two per thread) and their prefix sums
+  int64_t sum = 0;
+  int sl[2];
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
     const int b = 2 * tid + k;
     sl[k] = b < B ? seq_lens[b] : 0;
     sl[k] = sl[k] < 0 ? 0 : (sl[k] > max_seq_len ? max_seq_len : sl[k]);
-    cnt[k] = (sl[k] + CHUNK - 1) / CHUNK;
-    sum += cnt[k];
+    sum += sl[k];
   }
-  int incl = sum;
+  int64_t incl = sum;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
-    const int v = __shfl_up(incl, off);
+    const int64_t v = __shfl_up(incl, off);
     incl += lane >= off ? v : 0;
   }
   if (lane == 63) scan[wave] = incl;
   __syncthreads();
-  int run = incl - sum;
+  int64_t run = incl - sum;
 #pragma unroll
   for (int w2 = 0; w2 < WAVES; ++w2) run += w2 < wave ? scan[w2] : 0;
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
     if (2 * tid + k < B) pref[2 * tid + k] = run;
-    run += cnt[k];
+    run += sl[k];
   }
   if (tid == 0) {
-    int total = 0;
+    int64_t total = 0;
 #pragma unroll
     for (int w2 = 0; w2 < WAVES; ++w2) total += scan[w2];
     pref[B] = total;
   }
   __syncthreads();
 
-  const int64_t C = pref[B];
+  const int64_t K = pref[B];
   const int G = gridDim.x;
-  const int64_t cb = div_floor((int64_t)blockIdx.x * C, G);
-  const int64_t ce = div_floor((int64_t)(blockIdx.x + 1) * C, G);
+  const int64_t kb = div_floor((int64_t)blockIdx.x * K, G);
+  const int64_t ke = div_floor((int64_t)(blockIdx.x + 1) * K, G);
+  const int sub = lane >> 3, part = lane & 7;
   uint32_t acc = 0;
-  int b = 0;
-  while (b < B - 1 && pref[b + 1] <= cb) ++b;
-  for (; b < B && pref[b] < ce; ++b) {
-    const int x = (int)((cb > pref[b] ? cb : pref[b]) - pref[b]);
-    const int y = (int)((ce < pref[b + 1] ? ce : pref[b + 1]) - pref[b]);
-    const int len = seq_lens[b] < 0 ? 0 : (seq_lens[b] > max_seq_len ? max_seq_len : seq_lens[b]);
-    for (int p0 = x; p0 < y; p0 += PROBE_ROWS_LDS / CHUNK) {   // pieces of 4096 keys
-      const int p1 = p0 + PROBE_ROWS_LDS / CHUNK < y ? p0 + PROBE_ROWS_LDS / CHUNK : y;
-      __syncthreads();   // the previous piece's row ids are no longer read
-      for (int i = tid; i < PROBE_ROWS_LDS; i += THREADS) {
-        int u = p0 * CHUNK + i;
-        u = u < len - 1 ? u : len - 1;   // keys past the request repeat its last row
-        uint32_t un = (uint32_t)table[(int64_t)b * table_stride + (u >> shift)];
-        un = un < units ? un : units - 1;
-        rows[i] = (un << shift) + (uint32_t)(u & (page_size - 1));
-      }
-      __syncthreads();
-      // this wave's chunks of the piece: wave, wave + 8, ... with two in flight
-      const int nch = p1 - p0;
-      const int nloc = nch > wave ? (nch - wave + WAVES - 1) / WAVES : 0;
-      if (nloc > 0) {
-        const int last = nloc - 1;
-        auto rows_of = [&](int i) { return rows + (wave + (i < last ? i : last) * WAVES) * CHUNK; };
-        ProbeRows r0, r1;
-        probe_load(r0, kc, vc, rows_of(0), n, j);
-        probe_load(r1, kc, vc, rows_of(1), n, j);
-        int i = 0;
-        for (; i + 2 <= nloc; i += 2) {
-          acc ^= probe_fold(r0);
-          probe_load(r0, kc, vc, rows_of(i + 2), n, j);
-          acc ^= probe_fold(r1);
-          probe_load(r1, kc, vc, rows_of(i + 3), n, j);
+  for (int64_t p0 = kb; p0 < ke; p0 += PROBE_IDS) {
+    const int cnt = (int)(ke - p0 < PROBE_IDS ? ke - p0 : PROBE_IDS);
+    __syncthreads();   // the previous piece's row ids are no longer read
+    // this thread's keys p0 + tid + i * THREADS (clamped to the piece): their
+    // request by a binary search for the first and a walk for the rest, then
+    // every table load, then every store
+    int64_t key0 = p0 + (tid < cnt ? tid : cnt - 1);
+    int lo = 0, hi = B - 1;   // last request b with pref[b] <= key0
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (pref[mid] <= key0) lo = mid; else hi = mid - 1;
+    }
+    int b = lo;
+    const int32_t *src[PROBE_PER_THREAD];
+    int low[PROBE_PER_THREAD];
+#pragma unroll
+    for (int i = 0; i < PROBE_PER_THREAD; ++i) {
+      const int ki = tid + i * THREADS;
+      const int64_t key = p0 + (ki < cnt ? ki : cnt - 1);
+      while (b < B - 1 && pref[b + 1] <= key) ++b;
+      const int u = (int)(key - pref[b]);
+      src[i] = table + (int64_t)b * table_stride + (u >> shift);
+      low[i] = u & (page_size - 1);
+    }
+    int32_t ent[PROBE_PER_THREAD];
+#pragma unroll
+    for (int i = 0; i < PROBE_PER_THREAD; ++i) ent[i] = *src[i];
+#pragma unroll
+    for (int i = 0; i < PROBE_PER_THREAD; ++i) {
+      uint32_t un = (uint32_t)ent[i];
+      un = un < units ? un : units - 1;
+      const int ki = tid + i * THREADS;
+      if (ki < cnt) sid[ki] = (un << shift) + (uint32_t)low[i];
+    }
+    __syncthreads();
+
+    const int ng = (cnt + PROBE_KPG - 1) / PROBE_KPG;
+    const int gb = wave * ng / WAVES;
+    const int n = (wave + 1) * ng / WAVES - gb;
+    if (n > 0) {
+      // loads are unconditional (indices clamped into the share), so the
+      // compiler can count them and wait only for the group it folds next
+      auto issue = [&](ProbeGroup &grp, int g) {
+        const int gg = gb + (g < n ? g : n - 1);
+#pragma unroll
+        for (int u = 0; u < PROBE_BATCHES; ++u) {
+          int key = gg * PROBE_KPG + u * 8 + sub;
+          key = key < cnt ? key : cnt - 1;
+          const uint64_t r = sid[key];
+          grp.k[u] = *reinterpret_cast<const uint4 *>(kc + r * ROW + part * 16);
+          grp.v[u] = *reinterpret_cast<const uint4 *>(vc + r * ROW + part * 16);
         }
-        if (i < nloc) acc ^= probe_fold(r0);
+      };
+      auto fold = [&](const ProbeGroup &grp, int g) {
+#pragma unroll
+        for (int u = 0; u < PROBE_BATCHES; ++u) {
+          const int key = (gb + g) * PROBE_KPG + u * 8 + sub;
+          const uint32_t x = grp.k[u].x ^ grp.k[u].y ^ grp.k[u].z ^ grp.k[u].w ^ grp.v[u].x ^
+                             grp.v[u].y ^ grp.v[u].z ^ grp.v[u].w;
+          acc ^= key < cnt ? x : 0u;   // each key once
+        }
+      };
+      ProbeGroup ring[PROBE_RING];
+#pragma unroll
+      for (int s2 = 0; s2 < PROBE_RING; ++s2) issue(ring[s2], s2);
+      for (int it = 0; it < n; it += PROBE_RING) {
+#pragma unroll
+        for (int s2 = 0; s2 < PROBE_RING; ++s2) {
+          if (it + s2 < n) fold(ring[s2], it + s2);
+          issue(ring[s2], it + s2 + PROBE_RING);
+        }
       }
     }
   }
