@@ -222,8 +222,9 @@ int museattn_attn_step_noalloc(const void *qkv, const int32_t *positions, const 
  *   hidden    output features, a multiple of 64 in [64, MUSEATTN_MAX_HIDDEN]
  *   y         bf16 [T][hidden], 8-byte aligned, overlapping neither a nor o_weight
  *   stream    hipStream_t the work is enqueued on
- * Device pointers, owned by the caller.  Up to 159 tokens a kernel that keeps
- * rows of o in registers runs; from 160 tokens on, an LDS-tiled MFMA GEMM.
+ * Device pointers, owned by the caller.  Up to 63 tokens a kernel that keeps
+ * rows of o in registers runs; from 64 tokens on, an LDS-tiled MFMA GEMM
+ * whose tile shape is chosen from T and hidden.
  * Either way the call allocates nothing and keeps nothing between calls, so
  * any call (a shape's first included) can be captured into a graph.
  * Statuses: MUSEATTN_ERR_NULL, _PARAM (T or hidden), _ALIGN, _ALIAS, _LAUNCH. */

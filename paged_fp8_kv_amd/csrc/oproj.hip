@@ -98,9 +98,12 @@ __global__ __launch_bounds__(256) void oproj_kernel(const uint16_t *__restrict__
 }
 
 // From this many tokens on, the LDS-tiled GEMM (oproj_gemm.hip) runs the
-// projection: this kernel re-reads a once per 32 rows of o.
+// projection: this kernel re-reads a once per 32 rows of o, and its per-lane
+// loads keep fewer bytes in flight than the GEMM's direct-to-LDS ring
+// (hidden 8192, kernel times: T 32 6.8 vs 8.2 us, 64 8.9 vs 8.5, 128 14.6
+// vs 8.8).
 #ifndef MUSEATTN_OPROJ_GEMM_MIN_T
-#define MUSEATTN_OPROJ_GEMM_MIN_T 160
+#define MUSEATTN_OPROJ_GEMM_MIN_T 64
 #endif
 constexpr int OP_GEMM_MIN_T = MUSEATTN_OPROJ_GEMM_MIN_T;
 

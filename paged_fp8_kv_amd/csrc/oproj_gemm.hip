@@ -11,16 +11,21 @@
 //    o[row n][k + 8j .. +7]; B operand = 16 tokens of a, the same way; the
 //    D tile leaves y[token n][feature 4j .. 4j+3] in lane (n, j) (one 8-byte
 //    store);
-//  * K moves in stages of 32 through a ring of four LDS stages, filled by the
-//    gfx950 direct global -> LDS loads (global_load_lds_dwordx4: each lane's
-//    16 bytes land at LDS base + 16 * lane), so three stages are in flight
-//    while the waves multiply the fourth, without staging registers.  A
-//    stage holds 64-byte rows; the 16-byte slot s of row r holds K-chunk
-//    s ^ ((r / 2) % 4), so the 8 lanes of one ds_read_b128 pass (8
-//    consecutive rows, one chunk) hit distinct banks.  Each ring stage is its
-//    own __shared__ array and the K loop is unrolled by four, so the compiler
-//    sees which stage every load and LDS read touches and adds no waits of
-//    its own; one barrier per stage;
+//  * K moves in stages of BK (32 or 64) through a ring of four LDS stages,
+//    filled by the gfx950 direct global -> LDS loads (global_load_lds_dwordx4:
+//    each lane's 16 bytes land at LDS base + 16 * lane), so three stages are
+//    in flight while the waves multiply the fourth, without staging
+//    registers.  A stage holds rows of 2 BK bytes (4 or 8 chunks of 16 B);
+//    chunk c of row r sits at slot c ^ ((r / 2) % chunks), so each 16-lane
+//    pass of a ds_read_b128 (gfx950 serves lanes {0-3, 12-15, 20-23, 24-27},
+//    {4-7, 8-11, 16-19, 28-31} and the same + 32 together) meets 16 distinct
+//    16-byte bank groups.  Each ring stage is its own __shared__ array and the
+//    K loop is unrolled by four, so the compiler sees which stage every load
+//    and LDS read touches and adds no waits of its own; one barrier per
+//    stage.  64-element stages (whole 128-byte lines, 16 stages) serve the
+//    4-wave tiles: their K loop is bound by how many bytes a work-group has
+//    in flight, and 32-element stages left it at about 16 us whatever the
+//    tile;
 //  * work-group b takes feature tile b % tiles_m and token tile
 //    b / tiles_m: the 8 XCDs take work-groups round-robin, so each XCD's L2
 //    holds a few feature tiles of o against a few token tiles at a time.
@@ -32,8 +37,6 @@ namespace museattn {
 
 namespace {
 constexpr int GK = HQ * D;      // 1024: the contraction length
-constexpr int BK = 32;          // K per stage: one 16x16x32 K-step
-constexpr int RB = BK * 2;      // 64 bytes per staged row
 
 // Stage hand-over: every wave first waits for its own loads of the stage
 // (WAIT_VM: vmcnt only, gfx9 encoding with expcnt and lgkmcnt at their
@@ -44,14 +47,20 @@ constexpr int RB = BK * 2;      // 64 bytes per staged row
 #define WAIT_VM(v) \
   __builtin_amdgcn_s_waitcnt(((v) & 0xF) | (0x7 << 4) | (0xF << 8) | (((v) >> 4) << 14))
 
-template <int BM, int BN, int WAVES_M, int WAVES_N>
+template <int BM, int BN, int WAVES_M, int WAVES_N, int BK_>
 struct Cfg {
+  static constexpr int BK = BK_;             // K per stage (32 or 64)
+  static constexpr int RB = 2 * BK;          // bytes of one staged row
+  static constexpr int CPR = RB / 16;        // 16-byte chunks per row
+  static constexpr int RPI = 64 / CPR;       // rows one load instruction fills
+  static constexpr int KS = BK / 32;         // 16x16x32 K-steps per stage
   static constexpr int NW = WAVES_M * WAVES_N;
   static constexpr int NT = 64 * NW;
   static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   static constexpr int TM = WM / 16, TN = WN / 16;
-  static constexpr int NQ = (BM + BN) / (16 * NW);   // 16-row load instructions per wave and stage
-  static_assert((BM + BN) % (16 * NW) == 0 && WM % 16 == 0 && WN % 16 == 0, "tile shape");
+  static constexpr int NQ = (BM + BN) / (RPI * NW);   // load instructions per wave and stage
+  static_assert((BK == 32 || BK == 64) && (BM + BN) % (RPI * NW) == 0 && WM % 16 == 0 &&
+                    WN % 16 == 0, "tile shape");
   static constexpr int STAGE = (BM + BN) * RB;
 };
 
@@ -60,31 +69,39 @@ __device__ __forceinline__ void issue(uint8_t *base, const uint16_t *const (&src
                                       int wave) {
 #pragma unroll
   for (int q = 0; q < C::NQ; ++q)
-    __builtin_amdgcn_global_load_lds((const void *)(src[q] + kt * BK),
+    __builtin_amdgcn_global_load_lds((const void *)(src[q] + kt * C::BK),
                                      (__attribute__((address_space(3))) void *)(base + (C::NW * q + wave) * 1024),
                                      16, 0, 0);
 }
 
+// One stage's products: K-step ks reads chunk 4 ks + j of each of the
+// wave's rows (lane (n, j)); rd_a, rd_b: the lane's row offsets.
 template <class C>
-__device__ __forceinline__ void compute(const uint8_t *base, uint32_t rd_a, uint32_t rd_b,
-                                        f32x4 (&acc)[C::TM][C::TN]) {
-  bf16x8 af[C::TM], bfr[C::TN];
+__device__ __forceinline__ void compute(const uint8_t *base, uint32_t rd_a, uint32_t rd_b, int n,
+                                        int j, f32x4 (&acc)[C::TM][C::TN]) {
 #pragma unroll
-  for (int i = 0; i < C::TM; ++i) af[i] = *reinterpret_cast<const bf16x8 *>(base + rd_a + 16 * i * RB);
+  for (int ks = 0; ks < C::KS; ++ks) {
+    const uint32_t slot = 16 * ((4 * ks + j) ^ ((n >> 1) & (C::CPR - 1)));
+    bf16x8 af[C::TM], bfr[C::TN];
 #pragma unroll
-  for (int q = 0; q < C::TN; ++q) bfr[q] = *reinterpret_cast<const bf16x8 *>(base + rd_b + 16 * q * RB);
-#pragma unroll
-  for (int i = 0; i < C::TM; ++i)
+    for (int i = 0; i < C::TM; ++i)
+      af[i] = *reinterpret_cast<const bf16x8 *>(base + rd_a + slot + 16 * i * C::RB);
 #pragma unroll
     for (int q = 0; q < C::TN; ++q)
-      acc[i][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[q], acc[i][q], 0, 0, 0);
+      bfr[q] = *reinterpret_cast<const bf16x8 *>(base + rd_b + slot + 16 * q * C::RB);
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+      for (int q = 0; q < C::TN; ++q)
+        acc[i][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[q], acc[i][q], 0, 0, 0);
+  }
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N>
+template <int BM, int BN, int WAVES_M, int WAVES_N, int BK>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(const uint16_t *__restrict__ a,
                                              const uint16_t *__restrict__ o,
                                              uint16_t *__restrict__ y, int T, int N, int tiles_m) {
-  using C = Cfg<BM, BN, WAVES_M, WAVES_N>;
+  using C = Cfg<BM, BN, WAVES_M, WAVES_N, BK>;
   constexpr int NK = GK / BK;
   __shared__ __attribute__((aligned(1024))) uint8_t st0[C::STAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t st1[C::STAGE];
@@ -100,8 +117,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(const uint
   const uint16_t *src[C::NQ];
 #pragma unroll
   for (int q = 0; q < C::NQ; ++q) {
-    const int row = 16 * (C::NW * q + wave) + (lane >> 2);
-    const int c = (lane & 3) ^ ((lane >> 3) & 3);
+    const int row = C::RPI * (C::NW * q + wave) + lane / C::CPR;
+    const int c = (lane % C::CPR) ^ ((row >> 1) & (C::CPR - 1));
     const uint16_t *p;
     if (row < BM) {
       int r = m0 + row;
@@ -121,25 +138,24 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(const uint
 #pragma unroll
     for (int q = 0; q < C::TN; ++q) acc[i][q] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int slot = 16 * (j ^ ((n >> 1) & 3));
-  const uint32_t rd_a = (wm * C::WM + n) * RB + slot;
-  const uint32_t rd_b = (BM + wn * C::WN + n) * RB + slot;
+  const uint32_t rd_a = (wm * C::WM + n) * C::RB;
+  const uint32_t rd_b = (BM + wn * C::WN + n) * C::RB;
 
   issue<C>(st0, src, 0, wave);
   issue<C>(st1, src, 1, wave);
   issue<C>(st2, src, 2, wave);
 #pragma unroll 1
   for (int k0 = 0; k0 < NK - 4; k0 += 4) {
-    WAIT_VM(2 * C::NQ); LDS_BARRIER(); issue<C>(st3, src, k0 + 3, wave); compute<C>(st0, rd_a, rd_b, acc);
-    WAIT_VM(2 * C::NQ); LDS_BARRIER(); issue<C>(st0, src, k0 + 4, wave); compute<C>(st1, rd_a, rd_b, acc);
-    WAIT_VM(2 * C::NQ); LDS_BARRIER(); issue<C>(st1, src, k0 + 5, wave); compute<C>(st2, rd_a, rd_b, acc);
-    WAIT_VM(2 * C::NQ); LDS_BARRIER(); issue<C>(st2, src, k0 + 6, wave); compute<C>(st3, rd_a, rd_b, acc);
+    WAIT_VM(2 * C::NQ); LDS_BARRIER(); issue<C>(st3, src, k0 + 3, wave); compute<C>(st0, rd_a, rd_b, n, j, acc);
+    WAIT_VM(2 * C::NQ); LDS_BARRIER(); issue<C>(st0, src, k0 + 4, wave); compute<C>(st1, rd_a, rd_b, n, j, acc);
+    WAIT_VM(2 * C::NQ); LDS_BARRIER(); issue<C>(st1, src, k0 + 5, wave); compute<C>(st2, rd_a, rd_b, n, j, acc);
+    WAIT_VM(2 * C::NQ); LDS_BARRIER(); issue<C>(st2, src, k0 + 6, wave); compute<C>(st3, rd_a, rd_b, n, j, acc);
   }
   // the last four stages (NK-4 .. NK-2 already in flight)
-  WAIT_VM(2 * C::NQ); LDS_BARRIER(); issue<C>(st3, src, NK - 1, wave); compute<C>(st0, rd_a, rd_b, acc);
-  WAIT_VM(2 * C::NQ); LDS_BARRIER(); compute<C>(st1, rd_a, rd_b, acc);
-  WAIT_VM(1 * C::NQ); LDS_BARRIER(); compute<C>(st2, rd_a, rd_b, acc);
-  WAIT_VM(0); LDS_BARRIER(); compute<C>(st3, rd_a, rd_b, acc);
+  WAIT_VM(2 * C::NQ); LDS_BARRIER(); issue<C>(st3, src, NK - 1, wave); compute<C>(st0, rd_a, rd_b, n, j, acc);
+  WAIT_VM(2 * C::NQ); LDS_BARRIER(); compute<C>(st1, rd_a, rd_b, n, j, acc);
+  WAIT_VM(1 * C::NQ); LDS_BARRIER(); compute<C>(st2, rd_a, rd_b, n, j, acc);
+  WAIT_VM(0); LDS_BARRIER(); compute<C>(st3, rd_a, rd_b, n, j, acc);
 
 #pragma unroll
   for (int q = 0; q < C::TN; ++q) {
@@ -157,11 +173,11 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(const uint
     }
   }
 }
-template <int BM, int BN, int WAVES_M, int WAVES_N>
+template <int BM, int BN, int WAVES_M, int WAVES_N, int BK>
 void launch_gemm(const uint16_t *a, const uint16_t *o, uint16_t *y, int T, int N,
                  hipStream_t stream) {
   const int tiles_m = (N + BM - 1) / BM, tiles_n = (T + BN - 1) / BN;
-  hipLaunchKernelGGL((gemm_kernel<BM, BN, WAVES_M, WAVES_N>), dim3(tiles_m * tiles_n),
+  hipLaunchKernelGGL((gemm_kernel<BM, BN, WAVES_M, WAVES_N, BK>), dim3(tiles_m * tiles_n),
                      dim3(64 * WAVES_M * WAVES_N), 0, stream, a, o, y, T, N, tiles_m);
 }
 
@@ -171,15 +187,49 @@ int64_t tiles(int T, int N, int bm, int bn) {
 
 }  // namespace
 
-// 256 x 256 tiles (8 waves of 128 x 64, 128 KB of LDS, one work-group per
-// CU) once they give every one of the chip's 256 CUs a tile; otherwise
-// 128 x 128 (4 waves of 64 x 64, 64 KB, two work-groups per CU).
+#ifndef MUSEATTN_GEMM_CFG
+#define MUSEATTN_GEMM_CFG 0   // 0: chosen by shape; 1-5 force one tile shape
+#endif
+
+// Tile shapes (feature rows of o x tokens, waves):
+//   1: 256 x 256, 8 waves of 128 x 64, 32-element stages (128 KB of LDS)
+//   2: 128 x 128, 4 waves of 64 x 64, 64-element stages (128 KB)
+//   3: 128 x 64, 4 waves of 64 x 32, 64-element stages (96 KB)
+//   4: 128 x 192, 8 waves of 64 x 48, 64-element stages (160 KB)
+//   5: 256 x 128, 8 waves of 64 x 64, 32-element stages (96 KB)
+// Every shape takes one work-group per CU (LDS), so a launch runs in
+// ceil(tiles / 256) rounds on the chip's 256 CUs.  The shape with the least
+// estimated time wins, from the measured time of its first full round of
+// tiles and of each further round (hidden 8192; later rounds overlap the
+// previous round's tail): a partly filled round costs as much as a full one.
+static int gemm_cfg(int T, int N) {
+  if (MUSEATTN_GEMM_CFG) return MUSEATTN_GEMM_CFG;
+  struct Shape { int id, bm, bn; float first_us, next_us; };
+  static constexpr Shape shapes[] = {{3, 128, 64, 12.f, 11.f}, {2, 128, 128, 16.5f, 14.f},
+                                     {4, 128, 192, 19.f, 15.5f}, {5, 256, 128, 25.5f, 21.f},
+                                     {1, 256, 256, 41.f, 40.f}};
+  int best = 1;
+  float best_t = 0.f;
+  for (const Shape &sh : shapes) {
+    const int64_t rounds = (tiles(T, N, sh.bm, sh.bn) + 255) / 256;
+    const float t = sh.first_us + (float)(rounds - 1) * sh.next_us;
+    if (best_t == 0.f || t < best_t) {
+      best = sh.id;
+      best_t = t;
+    }
+  }
+  return best;
+}
+
 void gemm_oproj(const uint16_t *a, const uint16_t *o, uint16_t *y, int T, int N,
                 hipStream_t stream) {
-  if (tiles(T, N, 256, 256) >= 256)
-    launch_gemm<256, 256, 2, 4>(a, o, y, T, N, stream);
-  else
-    launch_gemm<128, 128, 2, 2>(a, o, y, T, N, stream);
+  switch (gemm_cfg(T, N)) {
+    case 1: launch_gemm<256, 256, 2, 4, 32>(a, o, y, T, N, stream); break;
+    case 5: launch_gemm<256, 128, 4, 2, 32>(a, o, y, T, N, stream); break;
+    case 4: launch_gemm<128, 192, 2, 4, 64>(a, o, y, T, N, stream); break;
+    case 2: launch_gemm<128, 128, 2, 2, 64>(a, o, y, T, N, stream); break;
+    default: launch_gemm<128, 64, 2, 2, 64>(a, o, y, T, N, stream); break;
+  }
 }
 
 }  // namespace museattn

@@ -30,18 +30,20 @@ def _need_gpu():
     P.lib()
 
 
-@pytest.mark.parametrize("T,hidden", [(1, 64), (7, 8192), (32, 8192), (33, 1088), (64, 8192),
-                                      (65, 64), (100, 2048), (129, 1088), (159, 1088),
-                                      (160, 8192), (256, 8192), (753, 8192), (1024, 64),
-                                      (1000, 1088), (2048, 8192), (13100, 1088)])
+@pytest.mark.parametrize("T,hidden", [(1, 64), (7, 8192), (32, 8192), (33, 1088), (63, 8192),
+                                      (64, 8192), (65, 64), (100, 2048), (129, 1088), (159, 1088),
+                                      (256, 8192), (384, 8192), (753, 8192), (1024, 64),
+                                      (1000, 1088), (1024, 8192), (2048, 8192), (3012, 8192),
+                                      (13100, 1088)])
 def test_oproj_alone(T, hidden):
-    """Up to 159 tokens the register kernel runs (32 rows of o per work-group,
-    64-token passes: T 33, 65, 100, 129 and 159 end inside a pass); from 160 on
-    the LDS-tiled GEMM (T 159 and 160 sit on either side of the switch).  The
-    GEMM's tiles: 128 x 64 (T 160, 256; T 1000 and hidden 1088, whose last
-    feature and token tiles are partial; hidden 64, half a tile), 128 x 128
-    (T 753) and 256 x 128 (T 2048; T 13100 with hidden 1088: partial tiles
-    on both axes)."""
+    """Up to 63 tokens the register kernel runs (32 rows of o per work-group,
+    64-token passes: T 7, 33 and 63 end inside a pass); from 64 on the
+    LDS-tiled GEMM (T 63 and 64 sit on either side of the switch).  The
+    GEMM's tile shapes: 128 x 64 (T 64 to 256 at hidden 8192; T 1000 and
+    hidden 1088, whose last feature and token tiles are partial; hidden 64,
+    half a tile), 128 x 128 (T 384), 128 x 192 (T 753 and 3012; T 13100 with
+    hidden 1088: partial tiles on both axes), 256 x 128 (T 1024) and 256 x
+    256 (T 2048)."""
     a = W.oproj_input(70 + T, T)
     o = W.oproj_weight(71, hidden)
     y = torch.empty(T, hidden, dtype=torch.bfloat16, device="cuda")
@@ -92,11 +94,11 @@ def test_step_then_oproj(case):
     compare_out(y.float().cpu().numpy(), want, f"{name} y")
 
 
-@pytest.mark.parametrize("T", [32, 753, 2048])
+@pytest.mark.parametrize("T", [32, 256, 753, 2048])
 def test_oproj_graph_replays_match_eager(T):
     """The projection captured into a HIP graph on its first call of the shape
     (the library keeps nothing between calls, so nothing has to be set up
-    first) -- the register kernel at 32 tokens, the GEMM at 753 and 2048 --
+    first) -- the register kernel at 32 tokens, the GEMM at 256, 753 and 2048 --
     gives the eager call's bytes on every replay, with eager calls in between."""
     a = W.oproj_input(90 + T, T).cuda()
     o = W.oproj_weight(91, 8192).cuda()
