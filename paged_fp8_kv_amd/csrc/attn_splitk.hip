@@ -31,6 +31,8 @@
 // 2): the block tokens x 8 heads of a KV group form a dense contraction on
 // fp16 MFMA over K/V staged in LDS (see the block section below); waves split
 // the KV heads, the column tiles and (verify) the sub-chunks.
+#include <type_traits>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -375,6 +377,110 @@ __device__ __forceinline__ f16x8 v_operand(const Stage &st, int sc, int dt, int 
   return __builtin_bit_cast(f16x8, v);
 }
 
+// Verify blocks stage the raw fp8 rows instead: a ring of VRING slots, each
+// one step of 64 keys (8 KB of K rows, then 8 KB of V rows, 128 B per key),
+// filled by the gfx950 direct global -> LDS loads (global_load_lds_dwordx4:
+// lane l's 16 bytes land at the wave's LDS base + 16 l).  Wave w loads keys
+// 8w..8w+7 of a step, 8 lanes per row; 16-byte chunk c of key x sits at slot
+// c ^ vswz(x).  The operands are converted to fp16 (exactly) as they are
+// read: K with ds_read_b64, V^T with the 8-bit transposing read
+// ds_read_b64_tr_b8 (within a 16-lane group, lane 2k + h names 8 bytes of
+// row k and lane i receives byte i of each of the 8 rows, probed on the GPU).
+// vswz keeps both kinds of read on distinct banks in each 32-lane pass: a K
+// read (16 keys of a tile, one chunk, both 8-byte halves) meets the 16
+// distinct 16-byte bank groups 8 (x % 2) + (c ^ vswz(x)), and so does a V^T
+// read (keys 4j..4j+3 and 16+4j..16+4j+3 for two adjacent j).  Half the LDS
+// bytes of the fp16 stage move per step, and no registers or VALU work go
+// into staging.
+// Wait for this wave's vector memory operations down to v outstanding
+// (vmcnt only; gfx9 encoding with expcnt and lgkmcnt at their maxima), and a
+// barrier without a fence (the memory clobber keeps LDS accesses on their
+// side of it).
+#define VM_WAIT(v) \
+  __builtin_amdgcn_s_waitcnt(((v) & 0xF) | (0x7 << 4) | (0xF << 8) | (((v) >> 4) << 14))
+#define LDS_BARRIER() asm volatile("s_barrier" ::: "memory")
+#ifndef MUSEATTN_VRING
+#define MUSEATTN_VRING 3
+#endif
+constexpr int VRING = MUSEATTN_VRING;     // ring slots: VRING - 1 steps in flight
+constexpr int VSLOT = STAGE_KEYS * ROW;   // bytes of one tensor's rows in a slot
+static_assert(VRING >= 3 && VRING <= 4, "ring depth");
+
+// Slot k of the ring: its own LDS object, so the compiler can tell the slot
+// an LDS read touches from the slots the loads still in flight fill.
+template <int K>
+__device__ __forceinline__ uint8_t *vring_slot() {
+  __shared__ __attribute__((aligned(1024))) uint8_t slot[2 * VSLOT];
+  return slot;
+}
+
+__device__ __forceinline__ int vswz(int x) { return ((x >> 1) & 7) ^ (((x >> 4) & 1) << 2); }
+
+// This thread's key of a step (wave w: keys 8w..8w+7, 8 lanes per key).
+__device__ __forceinline__ int vkey(int tid) { return 8 * (tid >> 6) + ((tid & 63) >> 3); }
+
+// The two direct loads (K row, V row) of this thread's 16 bytes of a step:
+// key vkey(tid), its chunk (lane % 8) ^ vswz(key) from cache row `row`.
+__device__ __forceinline__ void vring_issue(uint8_t *slot, const uint8_t *kc, const uint8_t *vc,
+                                            uint32_t row, int tid) {
+  const int c = (tid & 7) ^ vswz(vkey(tid));
+  const uint64_t off = (uint64_t)row * ROW + 16 * c;
+  uint8_t *dst = slot + 1024 * (tid >> 6);
+  __builtin_amdgcn_global_load_lds((const void *)(kc + off), (__attribute__((address_space(3))) void *)dst,
+                                   16, 0, 0);
+  __builtin_amdgcn_global_load_lds((const void *)(vc + off),
+                                   (__attribute__((address_space(3))) void *)(dst + VSLOT), 16, 0, 0);
+}
+
+// The operands of one sub-chunk from the fp8 ring, as 8 raw fp8 bytes each:
+//  * kr[2t + kk], the A operand of S^T for key tile t and K-step kk of KV head
+//    g: dims 32kk + 8j..+7 of key 32sc + 16t + n in lane (n, j);
+//  * vr[dt], the A operand of O^T = V^T . P^T for dim tile dt: lane (n, j)
+//    receives dim 16dt + n of keys 4j..4j+3 (bytes 0-3) and 16+4j..16+4j+3
+//    (bytes 4-7); it names 8 bytes (dims 16dt + 8 (n % 2)..) of the
+//    (n / 2)-th of those keys.
+// The 8 reads are issued in one asm block that waits for them itself: the
+// compiler would otherwise make every read of a slot wait for all the ring
+// loads in flight, since it cannot tell the slots apart once their code is
+// shared.  Every output is written only by the wait inside the block and
+// none overlaps an address input (early clobber).
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) const uint8_t lds_u8;
+__device__ __forceinline__ uint32_t lds_addr(const uint8_t *p) {
+  return (uint32_t)(uintptr_t)(lds_u8 *)p;
+}
+__device__ __forceinline__ void ring_operands(const uint8_t *slot, int sc, int n, int j, int g,
+                                              i32x2 (&kr)[4], i32x2 (&vr)[4]) {
+  uint32_t ka[4], va[4];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int x = 32 * sc + 16 * t + n, c = 4 * g + 2 * kk + (j >> 1);
+      ka[2 * t + kk] = lds_addr(slot + x * ROW + 16 * (c ^ vswz(x)) + 8 * (j & 1));
+    }
+  const int k = n >> 1;
+  const int xv = 32 * sc + (k < 4 ? 4 * j + k : 12 + 4 * j + k);
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+    va[dt] = lds_addr(slot + VSLOT + xv * ROW + 16 * ((4 * g + dt) ^ vswz(xv)) + 8 * (n & 1));
+  asm volatile(
+      "ds_read_b64 %0, %8\n\t"
+      "ds_read_b64 %1, %9\n\t"
+      "ds_read_b64 %2, %10\n\t"
+      "ds_read_b64 %3, %11\n\t"
+      "ds_read_b64_tr_b8 %4, %12\n\t"
+      "ds_read_b64_tr_b8 %5, %13\n\t"
+      "ds_read_b64_tr_b8 %6, %14\n\t"
+      "ds_read_b64_tr_b8 %7, %15\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(kr[0]), "=&v"(kr[1]), "=&v"(kr[2]), "=&v"(kr[3]), "=&v"(vr[0]), "=&v"(vr[1]),
+        "=&v"(vr[2]), "=&v"(vr[3])
+      : "v"(ka[0]), "v"(ka[1]), "v"(ka[2]), "v"(ka[3]), "v"(va[0]), "v"(va[1]), "v"(va[2]),
+        "v"(va[3])
+      : "memory");
+}
+
 // IEEE maximum (gfx950 v_maximum3_f32; no operand canonicalisation needed).
 __device__ __forceinline__ float fmax_ieee(float a, float b) { return __builtin_elementwise_maximum(a, b); }
 
@@ -454,6 +560,34 @@ __device__ __forceinline__ void block_subchunk(const Stage &stg, int sc, int u0,
     for (int kk = 0; kk < 2; ++kk) ka[t][kk] = k_operand(stg, sc, t, kk, n, j, g);
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) va[dt] = v_operand(stg, sc, dt, n, j, g);
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    if (c >= nc) break;   // uniform
+    f32x4 s0 = st.negm[c], s1 = st.negm[c];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[0][kk], qf[c][kk], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[1][kk], qf[c][kk], s1, 0, 0, 0);
+    }
+    block_tile(s0, s1, va, st.ones, u0, j, st, c);
+  }
+}
+
+// block_subchunk on a verify ring slot (fp8 rows, converted as read).
+__device__ __forceinline__ void block_subchunk8(const uint8_t *slot, int sc, int u0, int lane,
+                                                int g, int nc, const f16x8 (&qf)[2][2],
+                                                BlockState &st) {
+  const int n = lane & 15, j = lane >> 4;
+  i32x2 kr[4], vr[4];
+  ring_operands(slot, sc, n, j, g, kr, vr);
+  f16x8 ka[2][2], va[4];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+      ka[t][kk] = fp8x8_to_f16((uint32_t)kr[2 * t + kk][0], (uint32_t)kr[2 * t + kk][1]);
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) va[dt] = fp8x8_to_f16((uint32_t)vr[dt][0], (uint32_t)vr[dt][1]);
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
     if (c >= nc) break;   // uniform
@@ -680,7 +814,7 @@ struct Lds {
   union {
     float sm_o[WAVES][HQ][D];   // decode: the 8 waves' O per head
     float mrg[2][64][68];       // verify merge: chunk lane 1's O per KV head and column (padded)
-    Stage stg[MODE == 0 ? 1 : 2];   // verify and prefill: the K/V stage buffers
+    Stage stg[MODE == 3 ? 2 : 1];   // prefill: the K/V stage buffers (verify: a ring of its own)
   };
   float mrg_ml[2][64][2];       // verify merge: its (max, sum) per column
   QOps dq;                      // decode: the token's Q^T operands
@@ -932,11 +1066,12 @@ __device__ __forceinline__ void process_segment_block(const StepArgs &a, int b, 
   const int cs_tk = tid >> 5;   // sliding: this thread's RoPE pair is (token cs_tk, pair tid % 32)
   int posv = 0;
   if constexpr (VERIFY) posv = a.positions[b * a.L + ((lane & 7) < a.L ? (lane & 7) : a.L - 1)];
-  int eu[NR], eunit[NR];
+  constexpr int NE = VERIFY ? VRING - 1 : NR;   // steps whose loads may leave early
+  const int ekey = VERIFY ? vkey(tid) : stage_map(tid).key;
+  int eu[NE], eunit[NE];
 #pragma unroll
-  for (int k = 0; k < NR; ++k) {
-    const int v = r.kbase + x * CHUNK + (k < nsteps0 ? k : nsteps0 - 1) * STAGE_KEYS +
-                  stage_map(tid).key;
+  for (int k = 0; k < NE; ++k) {
+    const int v = r.kbase + x * CHUNK + (k < nsteps0 ? k : nsteps0 - 1) * STAGE_KEYS + ekey;
     eu[k] = v < r.klo ? r.klo : (v > r.khi ? r.khi : v);
     eunit[k] = a.table[(int64_t)b * a.table_stride + (eu[k] >> shift)];
   }
@@ -972,17 +1107,41 @@ __device__ __forceinline__ void process_segment_block(const StepArgs &a, int b, 
   }
   // The first steps' stage loads leave now, from the thread's own table
   // entries, so they overlap the set-up below -- unless the segment holds new
-  // rows, which must be written first.
-  const bool early = owned == 0;
+  // rows, which must be written first, or (verify) another segment of this
+  // work-group may still be reading the ring slots they fill.
+  const bool early = owned == 0 && (!VERIFY || first);
   const uint8_t *sbase = stage_base(a);
   StageIn in[NR];
+  uint4 ek0, ev0, ek1, ev1, ek2, ev2;   // verify: the first steps' rows, this thread's 16 B
   if (early) {
     const uint32_t units = (uint32_t)(a.num_rows >> shift);
+    uint32_t row[NE];
 #pragma unroll
-    for (int k = 0; k < NR; ++k) {
+    for (int k = 0; k < NE; ++k) {
       uint32_t un = (uint32_t)eunit[k];
       un = un < units ? un : units - 1;
-      stage_load_row(sbase, (un << shift) + (uint32_t)(eu[k] & (a.page_size - 1)), in[k]);
+      row[k] = (un << shift) + (uint32_t)(eu[k] & (a.page_size - 1));
+    }
+    if constexpr (VERIFY) {
+      // into registers: a direct load into LDS would be waited for at the
+      // set-up's first LDS access; the bytes go to their ring slots before
+      // the set-up barrier
+      const int c = (tid & 7) ^ vswz(ekey);
+      const uint8_t *k0 = a.k_cache + (uint64_t)row[0] * ROW + 16 * c;
+      const uint8_t *v0 = a.v_cache + (uint64_t)row[0] * ROW + 16 * c;
+      const uint8_t *k1 = a.k_cache + (uint64_t)row[1] * ROW + 16 * c;
+      const uint8_t *v1 = a.v_cache + (uint64_t)row[1] * ROW + 16 * c;
+      ek0 = *reinterpret_cast<const uint4 *>(k0);
+      ev0 = *reinterpret_cast<const uint4 *>(v0);
+      ek1 = *reinterpret_cast<const uint4 *>(k1);
+      ev1 = *reinterpret_cast<const uint4 *>(v1);
+      if constexpr (VRING > 3) {
+        ek2 = *reinterpret_cast<const uint4 *>(a.k_cache + (uint64_t)row[2] * ROW + 16 * c);
+        ev2 = *reinterpret_cast<const uint4 *>(a.v_cache + (uint64_t)row[2] * ROW + 16 * c);
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < NE; ++k) stage_load_row(sbase, row[k], in[k]);
     }
   }
 
@@ -1045,6 +1204,17 @@ __device__ __forceinline__ void process_segment_block(const StepArgs &a, int b, 
     // before this work-group's own loads.  (Prefill rows come from rows_kernel.)
     if (owned && wave < 4) write_new_rows<8>(a, b, owned, pos, sh.cs, rin);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    if (early) {   // the first steps' rows into their ring slots
+      const int o = 1024 * wave + 16 * lane;
+      *reinterpret_cast<uint4 *>(vring_slot<0>() + o) = ek0;
+      *reinterpret_cast<uint4 *>(vring_slot<0>() + VSLOT + o) = ev0;
+      *reinterpret_cast<uint4 *>(vring_slot<1>() + o) = ek1;
+      *reinterpret_cast<uint4 *>(vring_slot<1>() + VSLOT + o) = ev1;
+      if constexpr (VRING > 3) {
+        *reinterpret_cast<uint4 *>(vring_slot<2>() + o) = ek2;
+        *reinterpret_cast<uint4 *>(vring_slot<2>() + VSLOT + o) = ev2;
+      }
+    }
   }
   stamp(a, TS_QREADY, first);
   __syncthreads();   // the row ids (and verify's new rows) are in place
@@ -1063,48 +1233,91 @@ __device__ __forceinline__ void process_segment_block(const StepArgs &a, int b, 
       store_table(a, tn, sh.lrows);
       __syncthreads();
     }
-    // Steps of two sub-chunks.  The stage loads of step s go to register set
-    // s % NR, issued NR steps ahead; in the steady state they are
-    // unconditional (steps past the end are clamped to the last), so the
-    // compiler counts them and waits only for the set it stores next.
+    // Steps of two sub-chunks (64 keys).
     const int nsteps = (nch + 1) >> 1;
-    auto step_key = [&](int s) { return (s < nsteps ? s : nsteps - 1) * STAGE_KEYS; };
-    auto compute = [&](int s) {
-      const Stage &sg = sh.stg[s & 1];
-      if constexpr (VERIFY) {
-        if (2 * s + cl < nch && nc > 0)
-          block_subchunk(sg, cl, kstart + (2 * s + cl) * CHUNK, lane, g, nc, qf, st);
-      } else {
+    if constexpr (VERIFY) {
+      // The fp8 ring: step t fills slot t % VRING, VRING - 1 steps ahead.  At
+      // step t a wave waits for its own loads of t (the 2 (VRING - 2) of the
+      // later steps may stay in flight), the barrier makes everyone's visible
+      // and frees slot (t - 1) % VRING, which then takes step t + VRING - 1.
+      // Steps past the piece's end load its last step again (cache hits), so
+      // every wave issues the same loads and the counts hold.  The barrier is
+      // a bare s_barrier: a fence would also wait for the later steps' loads.
+      auto issue_step = [&](uint8_t *sl, int t) {
+        const int sk = (t < nsteps ? t : nsteps - 1) * STAGE_KEYS + vkey(tid);
+        vring_issue(sl, a.k_cache, a.v_cache, sh.lrows[sk], tid);
+      };
+      if (pc > 0 || !early) {   // uniform
+        issue_step(vring_slot<0>(), 0);
+        issue_step(vring_slot<1>(), 1);
+        if constexpr (VRING > 3) issue_step(vring_slot<2>(), 2);
+      }
+      // one step: slot RD holds it, slot WR takes step t + VRING - 1 (each
+      // slot named at compile time, so the compiler sees that the loads in
+      // flight fill other slots than the one read)
+      auto step = [&](auto rd_tag, auto wr_tag, int t) {
+        VM_WAIT(2 * (VRING - 2));
+        LDS_BARRIER();
+        issue_step(vring_slot<decltype(wr_tag)::value>(), t + VRING - 1);
+        if (2 * t + cl < nch && nc > 0)
+          block_subchunk8(vring_slot<decltype(rd_tag)::value>(), cl, kstart + (2 * t + cl) * CHUNK,
+                          lane, g, nc, qf, st);
+      };
+      using S0 = std::integral_constant<int, 0>;
+      using S1 = std::integral_constant<int, 1>;
+      using S2 = std::integral_constant<int, 2>;
+      using S3 = std::integral_constant<int, (VRING > 3 ? 3 : 2)>;
+      for (int s0 = 0; s0 < nsteps; s0 += VRING) {   // the branches are uniform
+        if constexpr (VRING == 3) {
+          step(S0{}, S2{}, s0);
+          if (s0 + 1 < nsteps) step(S1{}, S0{}, s0 + 1);
+          if (s0 + 2 < nsteps) step(S2{}, S1{}, s0 + 2);
+        } else {
+          step(S0{}, S3{}, s0);
+          if (s0 + 1 < nsteps) step(S1{}, S0{}, s0 + 1);
+          if (s0 + 2 < nsteps) step(S2{}, S1{}, s0 + 2);
+          if (s0 + 3 < nsteps) step(S3{}, S2{}, s0 + 3);
+        }
+      }
+      VM_WAIT(0);   // the loads past the piece's end are in before the slots are reused
+    } else {
+      // The stage loads of step s go to register set s % NR, issued NR steps
+      // ahead; in the steady state they are unconditional (steps past the end
+      // are clamped to the last), so the compiler counts them and waits only
+      // for the set it stores next.
+      auto step_key = [&](int s) { return (s < nsteps ? s : nsteps - 1) * STAGE_KEYS; };
+      auto compute = [&](int s) {
+        const Stage &sg = sh.stg[s & 1];
         if (nc > 0) {
           block_subchunk(sg, 0, kstart + 2 * s * CHUNK, lane, g, nc, qf, st);
           if (2 * s + 1 < nch)
             block_subchunk(sg, 1, kstart + (2 * s + 1) * CHUNK, lane, g, nc, qf, st);
         }
-      }
-    };
-    if (pc > 0 || !early) {   // uniform
+      };
+      if (pc > 0 || !early) {   // uniform
 #pragma unroll
-      for (int k = 0; k < NR; ++k) stage_load(sbase, sh.lrows, step_key(k), in[k]);
-    }
-    stage_store(in[0], sh.stg[0]);
-    stage_load(sbase, sh.lrows, step_key(NR), in[0]);
-    __syncthreads();
-    int s = 0;
-    for (; s + NR < nsteps; s += NR) {
+        for (int k = 0; k < NR; ++k) stage_load(sbase, sh.lrows, step_key(k), in[k]);
+      }
+      stage_store(in[0], sh.stg[0]);
+      stage_load(sbase, sh.lrows, step_key(NR), in[0]);
+      __syncthreads();
+      int s = 0;
+      for (; s + NR < nsteps; s += NR) {
+#pragma unroll
+        for (int k = 0; k < NR; ++k) {
+          compute(s + k);
+          stage_store(in[(k + 1) % NR], sh.stg[(s + k + 1) & 1]);
+          stage_load(sbase, sh.lrows, step_key(s + k + 1 + NR), in[(k + 1) % NR]);
+          __syncthreads();
+        }
+      }
 #pragma unroll
       for (int k = 0; k < NR; ++k) {
-        compute(s + k);
-        stage_store(in[(k + 1) % NR], sh.stg[(s + k + 1) & 1]);
-        stage_load(sbase, sh.lrows, step_key(s + k + 1 + NR), in[(k + 1) % NR]);
-        __syncthreads();
-      }
-    }
-#pragma unroll
-    for (int k = 0; k < NR; ++k) {
-      if (s + k < nsteps) {   // uniform
-        compute(s + k);
-        if (s + k + 1 < nsteps) stage_store(in[(k + 1) % NR], sh.stg[(s + k + 1) & 1]);
-        __syncthreads();
+        if (s + k < nsteps) {   // uniform
+          compute(s + k);
+          if (s + k + 1 < nsteps) stage_store(in[(k + 1) % NR], sh.stg[(s + k + 1) & 1]);
+          __syncthreads();
+        }
       }
     }
   }
