@@ -194,6 +194,25 @@ def test_verify_partition_invariance():
         assert (o.float() - outs[-1].float()).abs().max().item() <= 1.6e-2
 
 
+def test_verify_full_layer_partition_invariance():
+    """Full-layer verify blocks of 9K-12K keys: with one or five work-groups
+    a segment spans several 4096-key LDS fills of row ids, so the staging
+    ring crosses fill boundaries; with 64 the segments are short.  Every
+    count agrees with the oracle and with the default partition."""
+    w = W.make("vfull-partition", 8, 2, 8, (9000, 12000), W.FULL, 1, 1.0)
+    host = W.build_pools_numpy(w)
+    d = upload(w)
+    outs = []
+    for g in (1, 5, 64, 0):
+        log(f"[vfull-partition] work_groups={g}")
+        run(w, d, work_groups=g)
+        torch.cuda.synchronize()
+        full_check(w, d, host_pools=host)
+        outs.append(d["out"].clone())
+    for o in outs[:-1]:
+        assert (o.float() - outs[-1].float()).abs().max().item() <= 1.6e-2
+
+
 def test_many_requests_sharing_work_groups():
     """More requests than chunks per work-group: shares cross several request
     boundaries, so segments, partial slots and the last-contributor merge are
