@@ -39,7 +39,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 MFMA_F16_PEAK_TFLOPS = 2500.0
-OPROJ_GEMM_MIN_T = 160   # from this many tokens on the library runs the projection as its LDS-tiled GEMM
+OPROJ_GEMM_MIN_T = 64   # from this many tokens on the library runs the projection as its LDS-tiled GEMM
 OPROJ_HIDDEN = 8192   # the decoder layer's model width (the page's [T, 8192] activations)
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "attn_kernel_decode_b32_full_ctx60k-100k_pmc.txt")
 ATTN_SOURCE = os.path.join(ROOT, "paged_fp8_kv_amd", "csrc", "attn_splitk.hip")

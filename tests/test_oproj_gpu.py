@@ -120,3 +120,86 @@ def test_oproj_graph_replays_match_eager(T):
         P.oproj(a, o, y)   # eager work between replays
         torch.cuda.synchronize()
         assert torch.equal(y, eager)
+
+
+FUSED_CASES = [
+    # name, workload builder, hidden: every merge kind the step can end with,
+    # both projection kernels and hidden sizes from 64 to 16,384.
+    ("decode-b1-long-h8192", lambda: W.make("opf-decode-b1", 84, 1, 1, 20000, W.FULL, 1, 1.0), 8192),
+    ("decode-b3-h64", lambda: W.make("opf-decode-b3", 85, 3, 1, (1, 900), W.FULL, 64, 1.0), 64),
+    ("verify-b24-L2-sliding-h1088", lambda: W.make("opf-verify-b24", 86, 24, 2, (2100, 2600),
+                                                   W.SLIDING, 1, 1.0), 1088),
+    ("verify-b9-L7-full-h8192", lambda: W.make("opf-verify-b9", 87, 9, 7, (500, 1500), W.FULL, 1,
+                                               1.0), 8192),
+    ("verify-b8-L8-full-h8192", lambda: W.make("opf-verify-b8", 90, 8, 8, (500, 1500), W.FULL, 1,
+                                               1.0), 8192),
+    ("prefill-b5-L13-h8192", lambda: W.make("opf-prefill-b5", 88, 5, 13, (100, 400), W.FULL, 1,
+                                            1.0), 8192),
+    ("decode-b16-h16384", lambda: W.make("opf-decode-b16", 89, 16, 1, (300, 700), W.FULL, 1, 1.0),
+     16384),
+]
+
+
+@pytest.mark.parametrize("case", FUSED_CASES, ids=[c[0] for c in FUSED_CASES])
+def test_step_projection_matches_projection_alone(case):
+    """museattn_attn_step_oproj's y has the bytes museattn_oproj gives on the
+    step's output, after the per-(token, head) merge with short (B 3, 9, 16)
+    and long (B 1, 20,000 keys) slot lists and after the per-token merge (B 24,
+    L 2; prefill), on the register kernel (63 tokens nearly fill its one pass)
+    and on the GEMM (64, 65 tokens).  The step's output itself meets the
+    oracle's bar."""
+    name, build, hidden = case
+    w = build()
+    d = upload(w)
+    o = W.oproj_weight(92, hidden).cuda()
+    y = torch.full((w.T, hidden), float("nan"), dtype=torch.bfloat16, device="cuda")
+    log(f"[{name}] T={w.T} hidden={hidden}")
+    P.attn_step(d["qkv"], d["positions"], d["table"], d["seq_lens"], d["k_cache"], d["v_cache"],
+                w.kv_scale, w.page_size, w.layer_kind, d["out"], q_norm_w=d["w_q"],
+                k_norm_w=d["w_k"], o_norm_w=d["w_o"], max_seq_len=w.max_seq_len, eps=EPS,
+                q_scale=QS, rope_base=ROPE_BASE, o_weight=o, y=y)
+    alone = torch.empty_like(y)
+    P.oproj(d["out"].reshape(w.T, 1024), o, alone)
+    torch.cuda.synchronize()
+    assert torch.equal(y, alone), f"{name}: y differs from the projection of the step's output"
+    kb, vb = gpu_new_bytes(w, d)
+    out = oracle_out(w, kb, vb).reshape(w.T, 1024)
+    compare_out(d["out"].float().cpu().numpy().reshape(w.T, 1024), out, f"{name} out")
+
+
+def test_step_with_projection_graph_replays_match_eager():
+    """Decode B 32 followed by the projection, captured into a HIP graph on
+    the first call: every replay gives the eager call's y, with eager steps
+    in between."""
+    w = W.make("opf-graph", 93, 32, 1, (2000, 4000), W.FULL, 1, 1.0)
+    d = upload(w)
+    o = W.oproj_weight(94, 8192).cuda()
+    y = torch.empty(w.T, 8192, dtype=torch.bfloat16, device="cuda")
+
+    def step():
+        P.attn_step(d["qkv"], d["positions"], d["table"], d["seq_lens"], d["k_cache"],
+                    d["v_cache"], w.kv_scale, w.page_size, w.layer_kind, d["out"],
+                    q_norm_w=d["w_q"], k_norm_w=d["w_k"], o_norm_w=d["w_o"],
+                    max_seq_len=w.max_seq_len, eps=EPS, q_scale=QS, rope_base=ROPE_BASE,
+                    o_weight=o, y=y)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    eager = y.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for i in range(3):
+        y.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, eager), f"replay {i} differs from the eager step"
+        step()
+        torch.cuda.synchronize()
+        assert torch.equal(y, eager)
