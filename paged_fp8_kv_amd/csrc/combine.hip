@@ -19,9 +19,13 @@
 namespace museattn {
 
 // KB > 0: each slot lane loads its first KB slots in one batch (for units with
-// many slots: one long request spread over every work-group).
-template <int KB>
-__global__ __launch_bounds__(256) void combine_kernel(StepArgs a) {
+// many slots: one long request spread over every work-group).  SPEC (one
+// request, B = 1): the request's slots are work-groups 0 .. G - 1, so the
+// loads of slots sl, sl + 16, .., below nspec go out with the plan's instead
+// of after it (one memory round trip instead of two); the plan then selects
+// [s0, s1] among them, and slots from s = 16 KB on, if any, follow the plan.
+template <int KB, bool SPEC = false>
+__global__ __launch_bounds__(256) void combine_kernel(StepArgs a, int nspec) {
   __shared__ float sm_m[16], sm_l[16];
   __shared__ __attribute__((aligned(16))) float sm_o[16][D];
 
@@ -33,9 +37,39 @@ __global__ __launch_bounds__(256) void combine_kernel(StepArgs a) {
   const int b = t / a.L, jl = t % a.L;
   const int blk = jl / a.tb, jt = jl - blk * a.tb;
   const int u = b * a.nblk + blk, NU = a.nunits;
-  const int64_t p0 = a.plan[u], p1 = a.plan[u + 1];
-  const int G = a.plan[NU + 1];
-  const int64_t Ct = (int64_t)a.plan[NU] + (int64_t)NU * (a.seg_cost + a.end_cost);
+  const float2 *ml = reinterpret_cast<const float2 *>(a.part_ml);
+  const f32x4 *po = reinterpret_cast<const f32x4 *>(a.part_o);
+  auto entry = [&](int s) { return ((size_t)s * a.tb + jt) * HQ + h; };
+  const int sl = tid >> 4, dq = tid & 15;
+  int64_t p0, p1, pn;
+  int G;
+  float2 sv[SPEC ? KB : 1];
+  f32x4 sx[SPEC ? KB : 1];
+  if constexpr (SPEC) {
+    // vector loads (an atomic load is never a scalar one), so that the slot
+    // loads behind them are not held up by a wait for the plan
+    auto ldv = [](const int *p) {
+      return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
+    };
+    p0 = ldv(a.plan + u);
+    p1 = ldv(a.plan + u + 1);
+    pn = ldv(a.plan + NU);
+    G = ldv(a.plan + NU + 1);
+    // every candidate slot, clamped into [0, nspec): no branch, so no wait
+#pragma unroll
+    for (int k = 0; k < KB; ++k) {
+      const int sk = sl + 16 * k < nspec ? sl + 16 * k : nspec - 1;
+      const size_t e = entry(sk);
+      sv[k] = ml[e];
+      sx[k] = po[e * (D / 4) + dq];
+    }
+  } else {
+    p0 = a.plan[u];
+    p1 = a.plan[u + 1];
+    pn = a.plan[NU];
+    G = a.plan[NU + 1];
+  }
+  const int64_t Ct = pn + (int64_t)NU * (a.seg_cost + a.end_cost);
   const float g = bf16_bits_to_f32(a.qkv[(size_t)t * QKV_W + G_OFF + h * D + lane]);
   const float wo = a.wo[lane];
   // slots of unit u: w + u for the work-groups w whose cost share meets its
@@ -47,12 +81,8 @@ __global__ __launch_bounds__(256) void combine_kernel(StepArgs a) {
     s0 = wg_of_chunk(q0, Ct, G) + u;
     s1 = wg_of_chunk(q0 + (p1 - p0) - 1, Ct, G) + u;
   }
-  const float2 *ml = reinterpret_cast<const float2 *>(a.part_ml);
-  const f32x4 *po = reinterpret_cast<const f32x4 *>(a.part_o);
-  auto entry = [&](int s) { return ((size_t)s * a.tb + jt) * HQ + h; };
 
   // online merge of slots s0 + sl, s0 + sl + 16, ... (four loads in flight)
-  const int sl = tid >> 4, dq = tid & 15;
   float m = -INFINITY, l = 0.0f;
   f32x4 o = {0.f, 0.f, 0.f, 0.f};
   auto merge = [&](float2 v, f32x4 x) {
@@ -64,7 +94,26 @@ __global__ __launch_bounds__(256) void combine_kernel(StepArgs a) {
     m = mn;
   };
   int s = s0 + sl;
-  if constexpr (KB > 0) {
+  if constexpr (SPEC) {
+    // only this step's slots of the unit count (the others may hold anything)
+    bool keep[KB];
+#pragma unroll
+    for (int k = 0; k < KB; ++k) {
+      const int sk = sl + 16 * k;
+      keep[k] = sk >= s0 && sk <= s1 && sk < nspec && sv[k].x != -INFINITY;
+      if (keep[k]) m = fmaxf(m, sv[k].x);
+    }
+#pragma unroll
+    for (int k = 0; k < KB; ++k) {
+      if (keep[k]) {
+        const float c = __builtin_amdgcn_exp2f(sv[k].x - m);
+        l += sv[k].y * c;
+        o += sx[k] * c;
+      }
+    }
+    s = sl;   // the lane's first slot the batch did not cover
+    while (s < nspec || s < s0) s += 16;
+  } else if constexpr (KB > 0) {
     float2 v[KB];
     f32x4 x[KB];
 #pragma unroll
@@ -212,6 +261,15 @@ __global__ __launch_bounds__(256) void combine_tokens_kernel(StepArgs a) {
 #ifndef MUSEATTN_COMBINE_BATCH_SLOTS
 #define MUSEATTN_COMBINE_BATCH_SLOTS 48
 #endif
+// Most candidate slots a one-request merge loads with its plan (at most 3 per
+// slot lane).  With more, a work-group's partials are tens of KB, the merge is
+// bound by the bytes per CU rather than by round trips, and the unconditional
+// loads cost more than the round trip saves (graph-timed steps: 256 slots, 3f
+// 23.0 vs 22.0 us; 79, c1 11.6 vs 11.3; 31, c0 9.8 vs 10.5).
+#ifndef MUSEATTN_COMBINE_SPEC_SLOTS
+#define MUSEATTN_COMBINE_SPEC_SLOTS 48
+#endif
+static_assert(MUSEATTN_COMBINE_SPEC_SLOTS <= 48, "3 candidate slots per slot lane at most");
 #ifndef MUSEATTN_TOKENS_COMBINE_MIN_L
 #define MUSEATTN_TOKENS_COMBINE_MIN_L 2
 #endif
@@ -223,13 +281,25 @@ void launch_combine(const StepArgs &a, hipStream_t stream) {
   }
   // one request over many work-groups leaves many slots per unit: at most
   // one per work-group, and no more than its chunks (plus start-up) allow
-  const int64_t chunks = ((int64_t)a.max_seq_len + CHUNK - 1) / CHUNK + a.seg_cost + a.end_cost;
+  int64_t keys = a.max_seq_len;
+  if (a.sliding) keys = keys < WINDOW + a.L - 1 ? keys : WINDOW + a.L - 1;
+  const int64_t chunks = (keys + CHUNK - 1) / CHUNK + 1 + a.seg_cost + a.end_cost;
   const int64_t slots = a.B == 1 ? (chunks < a.work_groups ? chunks : a.work_groups)
                                  : a.work_groups / a.B + 2;
-  if (slots > MUSEATTN_COMBINE_BATCH_SLOTS)
-    hipLaunchKernelGGL(combine_kernel<16>, dim3(a.B * a.L * HQ), dim3(256), 0, stream, a);
-  else
-    hipLaunchKernelGGL(combine_kernel<0>, dim3(a.B * a.L * HQ), dim3(256), 0, stream, a);
+  const dim3 grid(a.B * a.L * HQ);
+  if (a.B == 1 && slots <= MUSEATTN_COMBINE_SPEC_SLOTS) {
+    // one request: its slots are work-groups 0 .. G - 1, G at most its cost
+    // (chunks, one more for a window's alignment, start-up and end costs)
+    const int nspec = (int)slots;
+    if (nspec <= 16)
+      hipLaunchKernelGGL((combine_kernel<1, true>), grid, dim3(256), 0, stream, a, nspec);
+    else
+      hipLaunchKernelGGL((combine_kernel<3, true>), grid, dim3(256), 0, stream, a, nspec);
+  } else if (slots > MUSEATTN_COMBINE_BATCH_SLOTS) {
+    hipLaunchKernelGGL((combine_kernel<16>), grid, dim3(256), 0, stream, a, 0);
+  } else {
+    hipLaunchKernelGGL((combine_kernel<0>), grid, dim3(256), 0, stream, a, 0);
+  }
 }
 
 }  // namespace museattn

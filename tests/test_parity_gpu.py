@@ -213,6 +213,31 @@ def test_verify_full_layer_partition_invariance():
         assert (o.float() - outs[-1].float()).abs().max().item() <= 1.6e-2
 
 
+@pytest.mark.parametrize("L,kind", [(1, W.FULL), (1, W.SLIDING), (8, W.FULL)],
+                         ids=["decode-full", "decode-sliding", "verify-L8-full"])
+def test_one_request_partition_invariance(L, kind):
+    """One request: with at most 48 candidate slots (work-groups 0 ..
+    min(work-groups, chunks + costs) - 1) its merge loads them all with its
+    plan and keeps those the plan names; with more it reads the plan first.
+    Work-group counts that give 1 and 3 candidates per slot lane (1, 5, 16;
+    17, 48) and counts past the switch (49 to 300 and the default) all agree
+    with the oracle and with each other."""
+    w = W.make(f"one-request-L{L}", 9 + L + kind, 1, L, 20000, kind, 1, 1.0)
+    host = W.build_pools_numpy(w)
+    d = upload(w)
+    outs = []
+    for g in (1, 5, 16, 17, 48, 49, 200, 256, 300, 0):
+        log(f"[one-request L={L} kind={kind}] work_groups={g}")
+        run(w, d, work_groups=g)
+        torch.cuda.synchronize()
+        full_check(w, d, host_pools=host)
+        outs.append(d["out"].clone())
+    for o in outs[:-1]:
+        assert (o.float() - outs[-1].float()).abs().max().item() <= 1.6e-2
+    run(w, d)
+    assert torch.equal(d["out"], outs[-1]), "two identical calls differ"
+
+
 def test_many_requests_sharing_work_groups():
     """More requests than chunks per work-group: shares cross several request
     boundaries, so segments, partial slots and the last-contributor merge are
