@@ -125,6 +125,11 @@ __device__ __forceinline__ float head_sum(float x) {
   return __int_as_float(q[0]) + __int_as_float(q[1]);
 }
 
+// NTV: V rows by non-temporal loads.  Each V load instruction reads 4 whole
+// rows (16 lanes x 8 bytes each); a K load reads half of each of 16 rows, the
+// other half coming from the next instruction, which finds the line in L2
+// only if the first one kept it -- so K keeps ordinary loads.
+template <bool NTV>
 __device__ __forceinline__ void load_rows(RowBuf &rb, const uint8_t *__restrict__ kc,
                                           const uint8_t *__restrict__ vc,
                                           const uint32_t *lrows, int n, int j) {
@@ -140,8 +145,10 @@ __device__ __forceinline__ void load_rows(RowBuf &rb, const uint8_t *__restrict_
   rb.k[3] = *reinterpret_cast<const uint4 *>(kp1 + 64);
   const uint32_t vr[8] = {va.x, va.y, va.z, va.w, vb.x, vb.y, vb.z, vb.w};
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
-    rb.v[i] = *reinterpret_cast<const uint2 *>(vc + (uint64_t)vr[i] * ROW + 8 * n);
+  for (int i = 0; i < 8; ++i) {
+    const uint8_t *vp = vc + (uint64_t)vr[i] * ROW + 8 * n;
+    rb.v[i] = NTV ? load_nt8(vp) : *reinterpret_cast<const uint2 *>(vp);
+  }
 }
 
 __device__ __forceinline__ void compute_chunk(const RowBuf &rb, int u0, int lane, TokState &st,
@@ -829,7 +836,7 @@ struct Lds {
 // One decode segment: chunks [x, y) of request b's key range (chunk i = keys
 // kbase + 32i ..), processed by the whole work-group, leaving one partial per
 // head in slot `slot`.  The 8 waves take interleaved chunks and both KV heads.
-template <int NBUF>
+template <int NBUF, bool NTV>
 __device__ __forceinline__ void process_segment(const StepArgs &a, int b, const KeyRange &r,
                                                 int p_tok, int x, int y, int slot, Lds<0> &sh,
                                                 bool first, bool second) {
@@ -844,7 +851,6 @@ __device__ __forceinline__ void process_segment(const StepArgs &a, int b, const 
   // piece's table entries, the token's q row and norm weights and the inputs
   // of its new k/v row (kept as raw bits: converting them here would wait for
   // the loads).  The token's position came with the plan (p_tok).
-  const int px1 = piece_x(1);
   TableIn tin;
   load_table_in(a, b, r, r.kbase + x * CHUNK, tin);
   // every wave loads q (wave 0 builds the Q^T operands) and the new row's
@@ -922,14 +928,14 @@ __device__ __forceinline__ void process_segment(const StepArgs &a, int b, const 
       RowBuf buf[NBUF];
 #pragma unroll
       for (int k = 0; k < NBUF; ++k)
-        load_rows(buf[k], a.k_cache, a.v_cache, rows_of(k < last ? k : last), n, j);
+        load_rows<NTV>(buf[k], a.k_cache, a.v_cache, rows_of(k < last ? k : last), n, j);
       int i = 0;
       for (; i + NBUF <= nloc; i += NBUF) {
 #pragma unroll
         for (int k = 0; k < NBUF; ++k) {
           compute_chunk(buf[k], key_of(i + k), lane, ts, sh.dq);
           const int inext = i + k + NBUF;
-          load_rows(buf[k], a.k_cache, a.v_cache, rows_of(inext < last ? inext : last), n, j);
+          load_rows<NTV>(buf[k], a.k_cache, a.v_cache, rows_of(inext < last ? inext : last), n, j);
         }
       }
 #pragma unroll
@@ -1392,7 +1398,7 @@ __device__ __forceinline__ void process_segment_block(const StepArgs &a, int b, 
 // processed one segment per unit; segment (w, u) writes its partial to slot
 // w + u (slots are unique because both w and u grow along the chunk space).
 // The combine kernel then merges each unit's slots.
-template <int MODE, int NBUF>
+template <int MODE, int NBUF, bool NTV = false>
 __global__ __launch_bounds__(THREADS, 2) void attn_kernel(StepArgs a) {
   __shared__ __attribute__((aligned(16))) Lds<MODE> sh;
   constexpr int MAXU = Lds<MODE>::MAXU;
@@ -1500,7 +1506,8 @@ __global__ __launch_bounds__(THREADS, 2) void attn_kernel(StepArgs a) {
     unit_of(a, u, b, blk);
     stamp(a, TS_SEG2_START, nsegs == 1);
     if constexpr (MODE == 0)
-      process_segment<NBUF>(a, b, r, sh.req_p0[u], x, y, w + u, sh, nsegs == 0, nsegs == 1);
+      process_segment<NBUF, NTV>(a, b, r, sh.req_p0[u], x, y, w + u, sh, nsegs == 0,
+                                 nsegs == 1);
     else
       process_segment_block<MODE>(a, b, blk, r, x, y, w + u, sh, nsegs == 0, nsegs == 1);
     ++nsegs;
@@ -1509,9 +1516,23 @@ __global__ __launch_bounds__(THREADS, 2) void attn_kernel(StepArgs a) {
   stamp(a, TS_EXIT);
 }
 
+// Decode steps whose rows may exceed this many bytes (B x the keys a request
+// may see x 256 B) read V by non-temporal loads.  Measured on decode B 32, contexts
+// U[60K, 100K] (672 MB per step, 2.6x the 256 MB Infinity Cache): attention
+// kernel 125 -> 115 us, at pools of 1.5 to 80 GB.  At B 16 (about 340 MB per
+// step) part of a step's rows is still cached at the next step, and the
+// ordinary loads were faster (61.0 vs 62.0 us).
+#ifndef MUSEATTN_NT_MIN_STEP_BYTES
+#define MUSEATTN_NT_MIN_STEP_BYTES (512ll << 20)
+#endif
+
 void launch_attn(const StepArgs &a, hipStream_t stream) {
   const dim3 grid(a.work_groups), block(THREADS);
-  if (a.L == 1)
+  const long long keys = a.sliding && a.max_seq_len > WINDOW ? WINDOW : a.max_seq_len;
+  const long long step_bytes = (long long)a.B * keys * 2 * ROW;
+  if (a.L == 1 && step_bytes > MUSEATTN_NT_MIN_STEP_BYTES)
+    hipLaunchKernelGGL((attn_kernel<0, MUSEATTN_DECODE_NBUF, true>), grid, block, 0, stream, a);
+  else if (a.L == 1)
     hipLaunchKernelGGL((attn_kernel<0, MUSEATTN_DECODE_NBUF>), grid, block, 0, stream, a);
   else if (a.L <= 8)
     hipLaunchKernelGGL((attn_kernel<2, 1>), grid, block, 0, stream, a);

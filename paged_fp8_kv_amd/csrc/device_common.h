@@ -28,6 +28,21 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+// Loads marked non-temporal (the "nt" cache policy): the line is read for
+// this access alone and is not kept for reuse.  For rows that one step reads
+// once, from a working set far larger than the caches, this gathers faster
+// than an ordinary load (which also fills the caches).
+__device__ __forceinline__ uint4 load_nt16(const uint8_t *p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint2 load_nt8(const uint8_t *p) {
+  const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(p));
+  return make_uint2(v.x, v.y);
+}
 
 // Everything one step's kernels read, passed by value.
 struct StepArgs {

@@ -12,8 +12,10 @@
 // trip); each wave then walks its own contiguous share in groups of 16 keys,
 // lane l reading bytes 16 (l % 8) .. + 15 of the K and V rows of key l / 8 of
 // a batch of 8 (8 lanes cover a 128-byte row), with two groups (8 KB per
-// wave) in flight.  Deeper rings, 16-wave or two-per-CU work-groups and
-// direct-to-LDS loads measured the same.
+// wave) in flight.  The row loads are non-temporal: each row is read once,
+// and not filling the caches with it made the gather 7-8% faster on decode B
+// 32 (672 MB of rows) and 1-3% at B 16.  Deeper rings, 16-wave or two-per-CU
+// work-groups and direct-to-LDS loads measured the same as this layout.
 #include "device_common.h"
 #include "launch.h"
 
@@ -132,8 +134,8 @@ __global__ __launch_bounds__(THREADS) void gather_probe_kernel(
           int key = gg * PROBE_KPG + u * 8 + sub;
           key = key < cnt ? key : cnt - 1;
           const uint64_t r = sid[key];
-          grp.k[u] = *reinterpret_cast<const uint4 *>(kc + r * ROW + part * 16);
-          grp.v[u] = *reinterpret_cast<const uint4 *>(vc + r * ROW + part * 16);
+          grp.k[u] = load_nt16(kc + r * ROW + part * 16);
+          grp.v[u] = load_nt16(vc + r * ROW + part * 16);
         }
       };
       auto fold = [&](const ProbeGroup &grp, int g) {
