@@ -12,8 +12,8 @@ import paged_fp8_kv_amd as P
 from oracle import museattn_oracle as O
 from paged_fp8_kv_amd import workloads as W
 
-from gpu_common import (EPS, compare_out, full_check, gpu_new_bytes, log, new_rows,
-                        oracle_prologue, run, upload)
+from gpu_common import (EPS, QS, ROPE_BASE, compare_out, full_check, gpu_new_bytes, log,
+                        new_rows, oracle_prologue, run, upload)
 
 pytestmark = pytest.mark.gpu
 
@@ -236,6 +236,36 @@ def test_one_request_partition_invariance(L, kind):
         assert (o.float() - outs[-1].float()).abs().max().item() <= 1.6e-2
     run(w, d)
     assert torch.equal(d["out"], outs[-1]), "two identical calls differ"
+
+
+@pytest.mark.parametrize("ps", [1, 64])
+def test_decode_nontemporal_loads_match(ps):
+    """A decode step that may read more than 512 MB of rows (B x max_seq_len x
+    256 B) loads V with non-temporal loads.  Declaring max_seq_len 300,000
+    for requests of 3K-9K keys selects that path at a size the oracle
+    checks: it gives the bytes of the ordinary loads (same arithmetic in the
+    same order) over several partitions, and meets the oracle."""
+    w = W.make(f"nt-decode-ps{ps}", 40 + ps, 8, 1, (3000, 9000), W.FULL, ps, 1.0)
+    host = W.build_pools_numpy(w)
+    d = upload(w)
+    msl = 300000
+    assert w.B * msl * 256 > 512 << 20 and w.B * w.max_seq_len * 256 < 512 << 20
+    stride = -(-msl // ps)
+    table = torch.full((w.B, stride), -1, dtype=torch.int32)
+    table[:, :w.table_stride] = torch.from_numpy(w.table)
+    table = table.cuda()
+    for g in (0, 7, 64):
+        log(f"[nt-decode ps={ps}] work_groups={g}")
+        run(w, d, work_groups=g)
+        torch.cuda.synchronize()
+        ordinary = d["out"].clone()
+        P.attn_step(d["qkv"], d["positions"], table, d["seq_lens"], d["k_cache"], d["v_cache"],
+                    w.kv_scale, w.page_size, w.layer_kind, d["out"], q_norm_w=d["w_q"],
+                    k_norm_w=d["w_k"], o_norm_w=d["w_o"], max_seq_len=msl, eps=EPS, q_scale=QS,
+                    rope_base=ROPE_BASE, work_groups=g)
+        torch.cuda.synchronize()
+        assert torch.equal(d["out"], ordinary), f"work_groups={g}: the two load paths differ"
+    full_check(w, d, host_pools=host)
 
 
 def test_many_requests_sharing_work_groups():
