@@ -74,7 +74,8 @@ def kernel_source_hash() -> str:
 def read_traffic(bytes_per_launch_alg):
     """HBM bytes per launch of the attention kernel from the committed PMC
     summary (FETCH_SIZE + WRITE_SIZE, scaled by a copy-kernel calibration), or
-    None when the summary is absent or was taken on another kernel source."""
+    None when the summary is absent, was taken on another kernel source or on
+    another workload (its algorithmic bytes per launch differ)."""
     if not os.path.exists(PMC_SUMMARY):
         return None
     vals = {}
@@ -85,10 +86,52 @@ def read_traffic(bytes_per_launch_alg):
                 vals[k.strip()] = v.strip()
     if vals.get("kernel_source_sha256") != kernel_source_hash():
         return None
+    if vals.get("algorithmic_bytes_per_launch") != str(int(bytes_per_launch_alg)):
+        return None
     try:
         return float(vals["hbm_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+# rocprofv3 MFMA counter summaries of the attention kernel, by workload
+# (SQ_VALU_MFMA_BUSY_CYCLES over the SIMDs' cycles), committed under profiles/
+MFMA_SUMMARIES = {
+    "2": "attn_kernel_decode_b32_full_ctx60k-100k_mfma.txt",
+    "3f": "attn_kernel_verify_b1_L8_full_ctx80k_mfma.txt",
+    "v32f": "attn_kernel_verify_b32_L8_full_ctx60k-100k_mfma_lds.txt",
+    "pf1f": "attn_kernel_prefill_b1_L753_full_ctx80k_mfma.txt",
+    "pff32": "attn_kernel_prefill_b1_L16384_full_ctx32k_mfma.txt",
+}
+
+
+def read_mfma_busy(cid, attn_flops):
+    """The attention kernel's MFMA busy fraction from the workload's committed
+    counter summary, or None when there is none, it was taken on another
+    kernel source, or its algorithmic FLOPs per dispatch are not this
+    workload's (within the summary's 4 printed digits)."""
+    name = MFMA_SUMMARIES.get(str(cid))
+    if name is None or not os.path.exists(os.path.join(ROOT, "profiles", name)):
+        return None
+    vals = {}
+    with open(os.path.join(ROOT, "profiles", name)) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    try:
+        busy = float(vals["mfma_busy_fraction"].split()[0])
+        if "algorithmic_flop_per_dispatch" in vals:
+            alg = float(vals["algorithmic_flop_per_dispatch"].split()[0])
+        else:   # "<counted>   (... x 512; algorithmic <flops>)"
+            alg = float(vals["mfma_flop_per_dispatch"].split("algorithmic")[1].strip(" )"))
+    except (KeyError, ValueError, IndexError):
+        return None
+    if abs(alg - attn_flops) > 5e-4 * attn_flops:
+        return None
+    return {"fraction": busy, "from": "profiles/" + name}
 
 
 def _oracle_job(job, barrier, results, index):
@@ -533,7 +576,8 @@ def main():
                     "unit": unit, "frac": round(achieved / peak, 4), "traffic": traffic,
                     "kernel": "attn_kernel (q/k norm, cache write, split-K attention)",
                     "algorithmic_bytes_per_launch": kv,
-                    "avg_launch_us": round(attn_avg_ms * 1e3, 2), "avg_launch_us_from": timing_note}
+                    "avg_launch_us": round(attn_avg_ms * 1e3, 2), "avg_launch_us_from": timing_note,
+                    "mfma_busy": read_mfma_busy(args.config, w.attn_flops)}
     else:
         # a prefill block: 4 * 64 FLOPs per (visible key, token, query head), an
         # fp16 MFMA contraction; each key's bytes are reused by up to L tokens
@@ -547,7 +591,8 @@ def main():
                     "kernel": "attn_kernel (split-K causal block attention; the new rows are "
                               "written by rows_kernel before it)",
                     "algorithmic_flops_per_launch": fl,
-                    "avg_launch_us": round(attn_avg_ms * 1e3, 2), "avg_launch_us_from": timing_note}
+                    "avg_launch_us": round(attn_avg_ms * 1e3, 2), "avg_launch_us_from": timing_note,
+                    "mfma_busy": read_mfma_busy(args.config, fl)}
 
     probe = None
     if w.L <= 8 and w.layer_kind == 0 and not args.no_gather_probe:
