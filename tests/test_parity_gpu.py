@@ -54,14 +54,40 @@ def test_config_parity_full_size(cid):
     """Full-size pools and batch in the launch configuration the bench times
     (config 2: 32 requests over ~80 GB of pools; config 4: 16 requests, page
     size 64, kv_scale 1/64): every output element of every request against
-    the oracle, every written byte within 1 ulp."""
+    the oracle, every written byte within 1 ulp; then graph replays of the
+    step, as the bench runs it, give the same bytes."""
     w = W.config(cid)
     log(f"[config {cid}] {w.name} B={w.B} pool rows={w.num_rows} checking all requests")
     d = upload(w)
-    run(w, d)
+    ws = torch.empty(P.workspace_bytes(w.B, w.L, w.max_seq_len, w.page_size, w.layer_kind),
+                     dtype=torch.uint8, device="cuda:0")
+    run(w, d, workspace=ws)
     torch.cuda.synchronize()
     full_check(w, d, requests=list(range(w.B)))
-    del d
+    # The launch configuration the benchmark times: several steps captured into
+    # one HIP graph and replayed; every replay leaves the checked call's bytes.
+    eager = d["out"].clone()
+    log(f"[config {cid}] graph replays")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        run(w, d, workspace=ws)     # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(4):
+            run(w, d, workspace=ws)
+    for i in range(3):
+        d["out"].zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(d["out"], eager), f"replay {i} differs from the checked call"
+        run(w, d, workspace=ws)     # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(d["out"], eager)
+    del g, d
     torch.cuda.empty_cache()
 
 
