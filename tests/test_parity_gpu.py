@@ -109,7 +109,7 @@ EDGE = [
     ("b2-L3-sliding", 2, 3, (2500, 3000), W.SLIDING, 1, 1.0),
     ("b2-L5-full", 2, 5, (900, 1300), W.FULL, 1, 1.0),
     ("b2-L7-sliding", 2, 7, (3000, 3100), W.SLIDING, 64, 1.0),
-    ("b33-full-spread", 33, 1, (15000, 25000), W.FULL, 1, 1.0),
+    ("b33-full-ctx25000-spread", 33, 1, (12500, 25000), W.FULL, 1, 1.0),
     ("b2-full-kv0.3", 2, 1, 500, W.FULL, 1, 0.3),
     ("b1-L8-ragged-tail", 1, 8, 4125, W.FULL, 1, 1.0),
 ]
