@@ -238,7 +238,34 @@ def _max_err_vs_library(case):
         got, _, _ = _run_oracle(w, kp.copy(), vp.copy())
     except Exception:
         return math.inf
-    return float(np.abs(got - want).max())
+    err = float(np.abs(got - want).max())
+    return err if math.isfinite(err) else math.inf   # NaN (sentinel rows read) is an error
+
+
+def _with_kw(fn, **over):
+    """fn with some keyword arguments forced (a planted mistake)."""
+    return lambda *a, **k: fn(*a, **{**k, **over})
+
+
+def _with_args(fn, over):
+    """fn with some positional arguments forced (a planted mistake)."""
+    def g(*a, **k):
+        a = list(a)
+        for i, v in over.items():
+            a[i] = v
+        return fn(*a, **k)
+    return g
+
+
+def _rope_interleaved(x, p, base):
+    """The other common RoPE layout, pairs (2i, 2i + 1): a plausible mix-up."""
+    x = np.asarray(x, dtype=np.float64)
+    th = O.rope_angles(p, base)
+    c, s = np.cos(th), np.sin(th)
+    a, b = x[..., 0::2], x[..., 1::2]
+    y = np.empty_like(x)
+    y[..., 0::2], y[..., 1::2] = a * c - b * s, b * c + a * s
+    return y
 
 
 MUTANTS = {
@@ -250,6 +277,25 @@ MUTANTS = {
                                             lambda p, w: (0 if w is None else max(0, p - (w - 1)), p + 1)),
     "rope sign": lambda mp: mp.setattr(O, "rope_angles", lambda p, base: -O.rope_inv_freq(base) * p),
     "gate not applied": lambda mp: mp.setattr(O, "sigmoid", lambda x: np.ones_like(x)),
+    "q scale dropped": lambda mp: mp.setattr(
+        O, "prologue", _with_kw(O.prologue, q_scale=1.0)),
+    "rope on full layers too": lambda mp: mp.setattr(
+        O, "prologue", _with_kw(O.prologue, rope=True)),
+    "kv_scale not applied on read": lambda mp: mp.setattr(
+        O, "attend", _with_args(O.attend, {8: 1.0})),
+    "rmsnorm sums instead of means": lambda mp: mp.setattr(
+        O, "rmsnorm", lambda x, w, eps: np.asarray(x, np.float64) / np.sqrt(
+            np.sum(np.asarray(x, np.float64) ** 2, axis=-1, keepdims=True) + eps) * w),
+    "output norm weight ignored": lambda mp: mp.setattr(
+        O, "gated_output", lambda a, gate, w_o, eps: O.rmsnorm(a, np.ones_like(w_o), eps)
+        * O.sigmoid(gate)),
+    "rope pairs adjacent dims": lambda mp: mp.setattr(O, "rope_neox", _rope_interleaved),
+    "k and v slices swapped": lambda mp: (mp.setattr(O, "K_OFF", O.V_OFF),
+                                          mp.setattr(O, "V_OFF", O.K_OFF)),
+    "page offset dropped": lambda mp: mp.setattr(
+        O, "cache_row", lambda table, b, u, ps: table[b, np.asarray(u, np.int64) // ps]
+        .astype(np.int64) * ps),
+    "new rows not written": lambda mp: mp.setattr(O, "write_rows", lambda *a, **k: None),
 }
 
 
