@@ -91,6 +91,26 @@ def test_config_parity_full_size(cid):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("cid,requests", [
+    ("v32f", (0, 9, 22, 31)), ("v16f", (0, 15)), ("d16f", (0, 7, 15)),
+    ("d32s", None), ("d16s", None), ("v32s", None), ("v16s", None)])
+def test_batch_shapes_full_size(cid, requests):
+    """The decode page's batch shapes (B 16 and 32, decode and verify blocks
+    of 8, sliding and full layers, contexts U[60K, 100K]) at full size in the
+    launch configuration the bench times: every written byte within 1 ulp,
+    and the outputs of sampled requests (full layers) or of every request
+    (sliding layers) against the oracle."""
+    w = W.config(cid)
+    reqs = list(range(w.B)) if requests is None else list(requests)
+    log(f"[batch {cid}] {w.name} B={w.B} L={w.L} checking requests {reqs}")
+    d = upload(w)
+    run(w, d)
+    torch.cuda.synchronize()
+    full_check(w, d, requests=reqs)
+    del d
+    torch.cuda.empty_cache()
+
+
 # ---------------------------------------------- edge cases and page's tests
 
 EDGE = [
