@@ -217,7 +217,9 @@ def attn_step(qkv, positions, table, seq_lens, k_cache, v_cache, kv_scale, page_
     need = workspace_bytes(B, L, max_seq_len, page_size, layer_kind, work_groups)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
-    _need(workspace.is_cuda and workspace.dtype == torch.uint8, "workspace must be a uint8 device tensor")
+    _need(workspace.is_cuda and workspace.device == dev and workspace.dtype == torch.uint8
+          and workspace.is_contiguous(),
+          f"workspace must be a contiguous uint8 tensor on {dev}")   # one span of numel bytes
     args = args + (workspace.data_ptr(), int(workspace.numel()))
     if o_weight is not None or y is not None:
         _need(o_weight is not None and y is not None, "o_weight and y go together")
