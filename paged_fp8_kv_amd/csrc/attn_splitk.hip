@@ -1525,12 +1525,19 @@ __global__ __launch_bounds__(THREADS, 2) void attn_kernel(StepArgs a) {
 #ifndef MUSEATTN_NT_MIN_STEP_BYTES
 #define MUSEATTN_NT_MIN_STEP_BYTES (512ll << 20)
 #endif
+// With 64-row pages the switch comes earlier: decode B 16, contexts U[60K,
+// 100K], page size 64 (331 MB per step): attention kernel 59.5 -> 58.0 us,
+// where at page size 1 (337 MB) the ordinary loads stay ahead (61.3 vs 61.8).
+#ifndef MUSEATTN_NT_MIN_STEP_BYTES_P64
+#define MUSEATTN_NT_MIN_STEP_BYTES_P64 (256ll << 20)
+#endif
 
 void launch_attn(const StepArgs &a, hipStream_t stream) {
   const dim3 grid(a.work_groups), block(THREADS);
   const long long keys = a.sliding && a.max_seq_len > WINDOW ? WINDOW : a.max_seq_len;
   const long long step_bytes = (long long)a.B * keys * 2 * ROW;
-  if (a.L == 1 && step_bytes > MUSEATTN_NT_MIN_STEP_BYTES)
+  const long long nt_min = a.page_size == 64 ? MUSEATTN_NT_MIN_STEP_BYTES_P64 : MUSEATTN_NT_MIN_STEP_BYTES;
+  if (a.L == 1 && step_bytes > nt_min)
     hipLaunchKernelGGL((attn_kernel<0, MUSEATTN_DECODE_NBUF, true>), grid, block, 0, stream, a);
   else if (a.L == 1)
     hipLaunchKernelGGL((attn_kernel<0, MUSEATTN_DECODE_NBUF>), grid, block, 0, stream, a);

@@ -287,15 +287,17 @@ def test_one_request_partition_invariance(L, kind):
 @pytest.mark.parametrize("ps", [1, 64])
 def test_decode_nontemporal_loads_match(ps):
     """A decode step that may read more than 512 MB of rows (B x max_seq_len x
-    256 B) loads V with non-temporal loads.  Declaring max_seq_len 300,000
-    for requests of 3K-9K keys selects that path at a size the oracle
-    checks: it gives the bytes of the ordinary loads (same arithmetic in the
-    same order) over several partitions, and meets the oracle."""
+    256 B; 256 MB at page size 64) loads V with non-temporal loads.
+    Declaring max_seq_len 300,000 for requests of 3K-9K keys selects that
+    path at a size the oracle checks: it gives the bytes of the ordinary
+    loads (same arithmetic in the same order) over several partitions, and
+    meets the oracle."""
     w = W.make(f"nt-decode-ps{ps}", 40 + ps, 8, 1, (3000, 9000), W.FULL, ps, 1.0)
     host = W.build_pools_numpy(w)
     d = upload(w)
     msl = 300000
-    assert w.B * msl * 256 > 512 << 20 and w.B * w.max_seq_len * 256 < 512 << 20
+    nt_min = (256 if ps == 64 else 512) << 20
+    assert w.B * msl * 256 > nt_min and w.B * w.max_seq_len * 256 < nt_min
     stride = -(-msl // ps)
     table = torch.full((w.B, stride), -1, dtype=torch.int32)
     table[:, :w.table_stride] = torch.from_numpy(w.table)
