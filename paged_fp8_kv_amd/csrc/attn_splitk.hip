@@ -40,9 +40,18 @@ namespace museattn {
 
 constexpr float LOG2E = 1.4426950408889634f;
 
-template <class T>
+// A partial's store.  NT: non-temporal, for decode steps that may read more
+// than 512 MB of rows: their partials are read once, by the merge kernel,
+// and need not sit in L2 at the kernel's end (decode B 32: step 116.7-117.7
+// -> 115.8-116.2 us).  Smaller steps keep ordinary stores, whose merge finds
+// them in L2 (paged decode B 16: 58.3-58.4 vs 58.9-59.2 us; sliding decode
+// B 1: 11.6-11.7 vs 12.0-12.1 us).
+template <bool NT = false, class T>
 __device__ __forceinline__ void part_store(T *p, T v) {
-  *p = v;
+  if constexpr (NT)
+    __builtin_nontemporal_store(v, p);
+  else
+    *p = v;
 }
 constexpr int MAX_SPLIT_LDS = 4096;   // table entries cached per work-group
 // log2 units a stale reference max may lag: P <= 2^15 stays inside fp16's
@@ -836,7 +845,7 @@ struct Lds {
 // One decode segment: chunks [x, y) of request b's key range (chunk i = keys
 // kbase + 32i ..), processed by the whole work-group, leaving one partial per
 // head in slot `slot`.  The 8 waves take interleaved chunks and both KV heads.
-template <int NBUF, bool NTV>
+template <int NBUF, bool NTV, bool NTP>
 __device__ __forceinline__ void process_segment(const StepArgs &a, int b, const KeyRange &r,
                                                 int p_tok, int x, int y, int slot, Lds<0> &sh,
                                                 bool first, bool second) {
@@ -982,9 +991,9 @@ __device__ __forceinline__ void process_segment(const StepArgs &a, int b, const 
     }
   }
   const size_t e = (size_t)slot * HQ + h;   // L = 1
-  part_store(reinterpret_cast<f32x2 *>(a.part_o + e * D + d2), o);
+  part_store<NTP>(reinterpret_cast<f32x2 *>(a.part_o + e * D + d2), o);
   if ((tid & 31) == 0) {
-    part_store(reinterpret_cast<f32x2 *>(a.part_ml + e * 2), f32x2{M, lt});
+    part_store<NTP>(reinterpret_cast<f32x2 *>(a.part_ml + e * 2), f32x2{M, lt});
   }
   stamp(a, TS_PARTIAL, first);
 }
@@ -1398,7 +1407,7 @@ __device__ __forceinline__ void process_segment_block(const StepArgs &a, int b, 
 // processed one segment per unit; segment (w, u) writes its partial to slot
 // w + u (slots are unique because both w and u grow along the chunk space).
 // The combine kernel then merges each unit's slots.
-template <int MODE, int NBUF, bool NTV = false>
+template <int MODE, int NBUF, bool NTV = false, bool NTP = false>
 __global__ __launch_bounds__(THREADS, 2) void attn_kernel(StepArgs a) {
   __shared__ __attribute__((aligned(16))) Lds<MODE> sh;
   constexpr int MAXU = Lds<MODE>::MAXU;
@@ -1506,7 +1515,7 @@ __global__ __launch_bounds__(THREADS, 2) void attn_kernel(StepArgs a) {
     unit_of(a, u, b, blk);
     stamp(a, TS_SEG2_START, nsegs == 1);
     if constexpr (MODE == 0)
-      process_segment<NBUF, NTV>(a, b, r, sh.req_p0[u], x, y, w + u, sh, nsegs == 0,
+      process_segment<NBUF, NTV, NTP>(a, b, r, sh.req_p0[u], x, y, w + u, sh, nsegs == 0,
                                  nsegs == 1);
     else
       process_segment_block<MODE>(a, b, blk, r, x, y, w + u, sh, nsegs == 0, nsegs == 1);
@@ -1537,7 +1546,9 @@ void launch_attn(const StepArgs &a, hipStream_t stream) {
   const long long keys = a.sliding && a.max_seq_len > WINDOW ? WINDOW : a.max_seq_len;
   const long long step_bytes = (long long)a.B * keys * 2 * ROW;
   const long long nt_min = a.page_size == 64 ? MUSEATTN_NT_MIN_STEP_BYTES_P64 : MUSEATTN_NT_MIN_STEP_BYTES;
-  if (a.L == 1 && step_bytes > nt_min)
+  if (a.L == 1 && step_bytes > MUSEATTN_NT_MIN_STEP_BYTES)
+    hipLaunchKernelGGL((attn_kernel<0, MUSEATTN_DECODE_NBUF, true, true>), grid, block, 0, stream, a);
+  else if (a.L == 1 && step_bytes > nt_min)
     hipLaunchKernelGGL((attn_kernel<0, MUSEATTN_DECODE_NBUF, true>), grid, block, 0, stream, a);
   else if (a.L == 1)
     hipLaunchKernelGGL((attn_kernel<0, MUSEATTN_DECODE_NBUF>), grid, block, 0, stream, a);

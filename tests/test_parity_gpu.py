@@ -284,18 +284,20 @@ def test_one_request_partition_invariance(L, kind):
     assert torch.equal(d["out"], outs[-1]), "two identical calls differ"
 
 
-@pytest.mark.parametrize("ps", [1, 64])
-def test_decode_nontemporal_loads_match(ps):
+@pytest.mark.parametrize("ps,msl", [(1, 300000), (64, 300000), (64, 200000)],
+                         ids=["ps1-586MB", "ps64-586MB", "ps64-391MB"])
+def test_decode_nontemporal_loads_match(ps, msl):
     """A decode step that may read more than 512 MB of rows (B x max_seq_len x
-    256 B; 256 MB at page size 64) loads V with non-temporal loads.
-    Declaring max_seq_len 300,000 for requests of 3K-9K keys selects that
-    path at a size the oracle checks: it gives the bytes of the ordinary
-    loads (same arithmetic in the same order) over several partitions, and
-    meets the oracle."""
+    256 B) loads V with non-temporal loads and stores its partials
+    non-temporally; at page size 64, from 256 MB, it loads V non-temporally
+    with ordinary partial stores.  Declaring a max_seq_len of 200,000 or
+    300,000 for requests of 3K-9K keys selects those paths at a size the
+    oracle checks: each gives the bytes of the ordinary path (same
+    arithmetic in the same order) over several partitions, and meets the
+    oracle."""
     w = W.make(f"nt-decode-ps{ps}", 40 + ps, 8, 1, (3000, 9000), W.FULL, ps, 1.0)
     host = W.build_pools_numpy(w)
     d = upload(w)
-    msl = 300000
     nt_min = (256 if ps == 64 else 512) << 20
     assert w.B * msl * 256 > nt_min and w.B * w.max_seq_len * 256 < nt_min
     stride = -(-msl // ps)
@@ -303,7 +305,7 @@ def test_decode_nontemporal_loads_match(ps):
     table[:, :w.table_stride] = torch.from_numpy(w.table)
     table = table.cuda()
     for g in (0, 7, 64):
-        log(f"[nt-decode ps={ps}] work_groups={g}")
+        log(f"[nt-decode ps={ps} max_seq_len={msl}] work_groups={g}")
         run(w, d, work_groups=g)
         torch.cuda.synchronize()
         ordinary = d["out"].clone()
