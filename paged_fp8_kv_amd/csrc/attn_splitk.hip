@@ -41,11 +41,11 @@ namespace museattn {
 constexpr float LOG2E = 1.4426950408889634f;
 
 // A partial's store.  NT: non-temporal, for decode steps that may read more
-// than 512 MB of rows: their partials are read once, by the merge kernel,
-// and need not sit in L2 at the kernel's end (decode B 32: step 116.7-117.7
-// -> 115.8-116.2 us).  Smaller steps keep ordinary stores, whose merge finds
-// them in L2 (paged decode B 16: 58.3-58.4 vs 58.9-59.2 us; sliding decode
-// B 1: 11.6-11.7 vs 12.0-12.1 us).
+// than 512 MB of rows and verify blocks from 4 MB: their partials are read
+// once, by the merge kernel, and need not sit in L2 at the kernel's end
+// (decode B 32: step 116.7-117.7 -> 115.8-116.2 us).  Smaller steps keep
+// ordinary stores, whose merge finds them in L2 (paged decode B 16: 58.3-58.4
+// vs 58.9-59.2 us; sliding decode B 1: 11.6-11.7 vs 12.0-12.1 us).
 template <bool NT = false, class T>
 __device__ __forceinline__ void part_store(T *p, T v) {
   if constexpr (NT)
@@ -1046,7 +1046,7 @@ __device__ __forceinline__ void q_values2(const StepArgs &a, const QIn2 &in, con
 // One segment of a verify (MODE 2) or prefill (MODE 3) block: chunks [x, y)
 // of unit (b, blk)'s key range, leaving one partial per (token, head) in slot
 // `slot`.
-template <int MODE>
+template <int MODE, bool NTP = false>
 __device__ __forceinline__ void process_segment_block(const StepArgs &a, int b, int blk,
                                                       const KeyRange &r, int x, int y, int slot,
                                                       Lds<MODE> &sh, bool first, bool second) {
@@ -1388,11 +1388,11 @@ __device__ __forceinline__ void process_segment_block(const StepArgs &a, int b, 
       if (tk >= nt) continue;
       const size_t e = ((size_t)slot * a.tb + tk) * HQ + 8 * g + (n & 7);
       if (j == 0) {
-        part_store(reinterpret_cast<f32x2 *>(a.part_ml + e * 2), f32x2{st.m[c], lsum[c]});
+        part_store<NTP>(reinterpret_cast<f32x2 *>(a.part_ml + e * 2), f32x2{st.m[c], lsum[c]});
       }
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
-        part_store(reinterpret_cast<f32x4 *>(a.part_o + e * D + 16 * dt + 4 * j), st.o[dt][c]);
+        part_store<NTP>(reinterpret_cast<f32x4 *>(a.part_o + e * D + 16 * dt + 4 * j), st.o[dt][c]);
     }
   }
   stamp(a, TS_PARTIAL, first);
@@ -1518,7 +1518,7 @@ __global__ __launch_bounds__(THREADS, 2) void attn_kernel(StepArgs a) {
       process_segment<NBUF, NTV, NTP>(a, b, r, sh.req_p0[u], x, y, w + u, sh, nsegs == 0,
                                  nsegs == 1);
     else
-      process_segment_block<MODE>(a, b, blk, r, x, y, w + u, sh, nsegs == 0, nsegs == 1);
+      process_segment_block<MODE, NTP>(a, b, blk, r, x, y, w + u, sh, nsegs == 0, nsegs == 1);
     ++nsegs;
   }
   stamp_count(a, TS_SEGMENTS, (uint64_t)nsegs);
@@ -1540,6 +1540,13 @@ __global__ __launch_bounds__(THREADS, 2) void attn_kernel(StepArgs a) {
 #ifndef MUSEATTN_NT_MIN_STEP_BYTES_P64
 #define MUSEATTN_NT_MIN_STEP_BYTES_P64 (256ll << 20)
 #endif
+// Verify blocks store their partials (8 tokens' worth per slot) non-temporally
+// from this many bytes of rows per step: verify L 8 over 80K keys 22.6 ->
+// 22.3 us per step, B 32 full 161.8 -> 158.7, B 32 sliding 23.2 -> 22.5; a
+// sliding block of one request (0.5 MB) was slower with them (16.3 vs 16.8).
+#ifndef MUSEATTN_NTP_MIN_VERIFY_BYTES
+#define MUSEATTN_NTP_MIN_VERIFY_BYTES (4ll << 20)
+#endif
 
 void launch_attn(const StepArgs &a, hipStream_t stream) {
   const dim3 grid(a.work_groups), block(THREADS);
@@ -1552,6 +1559,8 @@ void launch_attn(const StepArgs &a, hipStream_t stream) {
     hipLaunchKernelGGL((attn_kernel<0, MUSEATTN_DECODE_NBUF, true>), grid, block, 0, stream, a);
   else if (a.L == 1)
     hipLaunchKernelGGL((attn_kernel<0, MUSEATTN_DECODE_NBUF>), grid, block, 0, stream, a);
+  else if (a.L <= 8 && step_bytes > MUSEATTN_NTP_MIN_VERIFY_BYTES)
+    hipLaunchKernelGGL((attn_kernel<2, 1, false, true>), grid, block, 0, stream, a);
   else if (a.L <= 8)
     hipLaunchKernelGGL((attn_kernel<2, 1>), grid, block, 0, stream, a);
   else

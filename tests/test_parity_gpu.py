@@ -284,28 +284,30 @@ def test_one_request_partition_invariance(L, kind):
     assert torch.equal(d["out"], outs[-1]), "two identical calls differ"
 
 
-@pytest.mark.parametrize("ps,msl", [(1, 300000), (64, 300000), (64, 200000)],
-                         ids=["ps1-586MB", "ps64-586MB", "ps64-391MB"])
-def test_decode_nontemporal_loads_match(ps, msl):
-    """A decode step that may read more than 512 MB of rows (B x max_seq_len x
-    256 B) loads V with non-temporal loads and stores its partials
-    non-temporally; at page size 64, from 256 MB, it loads V non-temporally
-    with ordinary partial stores.  Declaring a max_seq_len of 200,000 or
-    300,000 for requests of 3K-9K keys selects those paths at a size the
-    oracle checks: each gives the bytes of the ordinary path (same
-    arithmetic in the same order) over several partitions, and meets the
-    oracle."""
-    w = W.make(f"nt-decode-ps{ps}", 40 + ps, 8, 1, (3000, 9000), W.FULL, ps, 1.0)
+@pytest.mark.parametrize("L,B,ctx,ps,msl", [
+    (1, 8, (3000, 9000), 1, 300000), (1, 8, (3000, 9000), 64, 300000),
+    (1, 8, (3000, 9000), 64, 200000), (8, 1, 5000, 1, 300000), (8, 2, 4000, 64, 300000)],
+    ids=["decode-ps1-586MB", "decode-ps64-586MB", "decode-ps64-391MB", "verify-ps1", "verify-ps64"])
+def test_nontemporal_paths_match(L, B, ctx, ps, msl):
+    """The paths chosen by the step's size: a decode step that may read more
+    than 512 MB of rows (B x max_seq_len x 256 B) loads V and stores its
+    partials non-temporally; at page size 64, from 256 MB, it loads V
+    non-temporally with ordinary partial stores; a verify block from 4 MB
+    stores its partials non-temporally.  Declaring a larger max_seq_len for
+    small requests selects those paths at a size the oracle checks: each
+    gives the bytes of the ordinary path (same arithmetic in the same order)
+    over several partitions, and meets the oracle."""
+    w = W.make(f"nt-L{L}-ps{ps}", 40 + ps + L, B, L, ctx, W.FULL, ps, 1.0)
     host = W.build_pools_numpy(w)
     d = upload(w)
-    nt_min = (256 if ps == 64 else 512) << 20
+    nt_min = (4 if L > 1 else 256 if ps == 64 else 512) << 20
     assert w.B * msl * 256 > nt_min and w.B * w.max_seq_len * 256 < nt_min
     stride = -(-msl // ps)
     table = torch.full((w.B, stride), -1, dtype=torch.int32)
     table[:, :w.table_stride] = torch.from_numpy(w.table)
     table = table.cuda()
     for g in (0, 7, 64):
-        log(f"[nt-decode ps={ps} max_seq_len={msl}] work_groups={g}")
+        log(f"[nt L={L} ps={ps} max_seq_len={msl}] work_groups={g}")
         run(w, d, work_groups=g)
         torch.cuda.synchronize()
         ordinary = d["out"].clone()
