@@ -1406,7 +1406,9 @@ __device__ __forceinline__ void process_segment_block(const StepArgs &a, int b, 
 // another still has a long split.  A share that crosses unit boundaries is
 // processed one segment per unit; segment (w, u) writes its partial to slot
 // w + u (slots are unique because both w and u grow along the chunk space).
-// The combine kernel then merges each unit's slots.
+// The combine kernel then merges each unit's slots.  NTV and NTP: V rows
+// read and partials stored non-temporally (decode; NTP also verify), chosen
+// by launch_attn from the step's size.
 template <int MODE, int NBUF, bool NTV = false, bool NTP = false>
 __global__ __launch_bounds__(THREADS, 2) void attn_kernel(StepArgs a) {
   __shared__ __attribute__((aligned(16))) Lds<MODE> sh;
@@ -1526,11 +1528,12 @@ __global__ __launch_bounds__(THREADS, 2) void attn_kernel(StepArgs a) {
 }
 
 // Decode steps whose rows may exceed this many bytes (B x the keys a request
-// may see x 256 B) read V by non-temporal loads.  Measured on decode B 32, contexts
-// U[60K, 100K] (672 MB per step, 2.6x the 256 MB Infinity Cache): attention
-// kernel 125 -> 115 us, at pools of 1.5 to 80 GB.  At B 16 (about 340 MB per
-// step) part of a step's rows is still cached at the next step, and the
-// ordinary loads were faster (61.0 vs 62.0 us).
+// may see x 256 B) read V by non-temporal loads and store their partials
+// non-temporally.  Measured on decode B 32, contexts U[60K, 100K] (672 MB per
+// step, 2.6x the 256 MB Infinity Cache): attention kernel 125 -> 115 us, at
+// pools of 1.5 to 80 GB.  At B 16 (about 340 MB per step) part of a step's
+// rows is still cached at the next step, and the ordinary loads were faster
+// (61.0 vs 62.0 us).
 #ifndef MUSEATTN_NT_MIN_STEP_BYTES
 #define MUSEATTN_NT_MIN_STEP_BYTES (512ll << 20)
 #endif
