@@ -437,15 +437,18 @@ __device__ __forceinline__ int vkey(int tid) { return 8 * (tid >> 6) + ((tid & 6
 
 // The two direct loads (K row, V row) of this thread's 16 bytes of a step:
 // key vkey(tid), its chunk (lane % 8) ^ vswz(key) from cache row `row`.
+// AUX: the loads' cache-policy bits (2: non-temporal; each load instruction
+// reads 8 whole rows, so no line is wanted again by a later one).
+template <int AUX>
 __device__ __forceinline__ void vring_issue(uint8_t *slot, const uint8_t *kc, const uint8_t *vc,
                                             uint32_t row, int tid) {
   const int c = (tid & 7) ^ vswz(vkey(tid));
   const uint64_t off = (uint64_t)row * ROW + 16 * c;
   uint8_t *dst = slot + 1024 * (tid >> 6);
   __builtin_amdgcn_global_load_lds((const void *)(kc + off), (__attribute__((address_space(3))) void *)dst,
-                                   16, 0, 0);
+                                   16, 0, AUX);
   __builtin_amdgcn_global_load_lds((const void *)(vc + off),
-                                   (__attribute__((address_space(3))) void *)(dst + VSLOT), 16, 0, 0);
+                                   (__attribute__((address_space(3))) void *)(dst + VSLOT), 16, 0, AUX);
 }
 
 // The operands of one sub-chunk from the fp8 ring, as 8 raw fp8 bytes each:
@@ -1046,7 +1049,7 @@ __device__ __forceinline__ void q_values2(const StepArgs &a, const QIn2 &in, con
 // One segment of a verify (MODE 2) or prefill (MODE 3) block: chunks [x, y)
 // of unit (b, blk)'s key range, leaving one partial per (token, head) in slot
 // `slot`.
-template <int MODE, bool NTP = false>
+template <int MODE, bool NTP = false, bool NTV = false>
 __device__ __forceinline__ void process_segment_block(const StepArgs &a, int b, int blk,
                                                       const KeyRange &r, int x, int y, int slot,
                                                       Lds<MODE> &sh, bool first, bool second) {
@@ -1260,7 +1263,7 @@ __device__ __forceinline__ void process_segment_block(const StepArgs &a, int b, 
       // a bare s_barrier: a fence would also wait for the later steps' loads.
       auto issue_step = [&](uint8_t *sl, int t) {
         const int sk = (t < nsteps ? t : nsteps - 1) * STAGE_KEYS + vkey(tid);
-        vring_issue(sl, a.k_cache, a.v_cache, sh.lrows[sk], tid);
+        vring_issue<NTV ? 2 : 0>(sl, a.k_cache, a.v_cache, sh.lrows[sk], tid);
       };
       if (pc > 0 || !early) {   // uniform
         issue_step(vring_slot<0>(), 0);
@@ -1406,9 +1409,9 @@ __device__ __forceinline__ void process_segment_block(const StepArgs &a, int b, 
 // another still has a long split.  A share that crosses unit boundaries is
 // processed one segment per unit; segment (w, u) writes its partial to slot
 // w + u (slots are unique because both w and u grow along the chunk space).
-// The combine kernel then merges each unit's slots.  NTV and NTP: V rows
-// read and partials stored non-temporally (decode; NTP also verify), chosen
-// by launch_attn from the step's size.
+// The combine kernel then merges each unit's slots.  NTV and NTP: rows read
+// (decode: V; verify: K and V into the ring) and partials stored
+// non-temporally, chosen by launch_attn from the step's size.
 template <int MODE, int NBUF, bool NTV = false, bool NTP = false>
 __global__ __launch_bounds__(THREADS, 2) void attn_kernel(StepArgs a) {
   __shared__ __attribute__((aligned(16))) Lds<MODE> sh;
@@ -1520,7 +1523,8 @@ __global__ __launch_bounds__(THREADS, 2) void attn_kernel(StepArgs a) {
       process_segment<NBUF, NTV, NTP>(a, b, r, sh.req_p0[u], x, y, w + u, sh, nsegs == 0,
                                  nsegs == 1);
     else
-      process_segment_block<MODE, NTP>(a, b, blk, r, x, y, w + u, sh, nsegs == 0, nsegs == 1);
+      process_segment_block<MODE, NTP, NTV>(a, b, blk, r, x, y, w + u, sh, nsegs == 0,
+                                            nsegs == 1);
     ++nsegs;
   }
   stamp_count(a, TS_SEGMENTS, (uint64_t)nsegs);
@@ -1529,7 +1533,8 @@ __global__ __launch_bounds__(THREADS, 2) void attn_kernel(StepArgs a) {
 
 // Decode steps whose rows may exceed this many bytes (B x the keys a request
 // may see x 256 B) read V by non-temporal loads and store their partials
-// non-temporally.  Measured on decode B 32, contexts U[60K, 100K] (672 MB per
+// non-temporally; verify steps read K and V into their ring non-temporally
+// (verify B 32, L 8: step 161.6 -> 156.4 us; at B 16, 410 MB, no gain).  Measured on decode B 32, contexts U[60K, 100K] (672 MB per
 // step, 2.6x the 256 MB Infinity Cache): attention kernel 125 -> 115 us, at
 // pools of 1.5 to 80 GB.  At B 16 (about 340 MB per step) part of a step's
 // rows is still cached at the next step, and the ordinary loads were faster
@@ -1562,6 +1567,8 @@ void launch_attn(const StepArgs &a, hipStream_t stream) {
     hipLaunchKernelGGL((attn_kernel<0, MUSEATTN_DECODE_NBUF, true>), grid, block, 0, stream, a);
   else if (a.L == 1)
     hipLaunchKernelGGL((attn_kernel<0, MUSEATTN_DECODE_NBUF>), grid, block, 0, stream, a);
+  else if (a.L <= 8 && step_bytes > MUSEATTN_NT_MIN_STEP_BYTES)
+    hipLaunchKernelGGL((attn_kernel<2, 1, true, true>), grid, block, 0, stream, a);
   else if (a.L <= 8 && step_bytes > MUSEATTN_NTP_MIN_VERIFY_BYTES)
     hipLaunchKernelGGL((attn_kernel<2, 1, false, true>), grid, block, 0, stream, a);
   else if (a.L <= 8)

@@ -286,14 +286,17 @@ def test_one_request_partition_invariance(L, kind):
 
 @pytest.mark.parametrize("L,B,ctx,ps,msl", [
     (1, 8, (3000, 9000), 1, 300000), (1, 8, (3000, 9000), 64, 300000),
-    (1, 8, (3000, 9000), 64, 200000), (8, 1, 5000, 1, 300000), (8, 2, 4000, 64, 300000)],
-    ids=["decode-ps1-586MB", "decode-ps64-586MB", "decode-ps64-391MB", "verify-ps1", "verify-ps64"])
+    (1, 8, (3000, 9000), 64, 200000), (8, 1, 5000, 1, 300000), (8, 2, 4000, 64, 300000),
+    (8, 8, 1500, 1, 300000)],
+    ids=["decode-ps1-586MB", "decode-ps64-586MB", "decode-ps64-391MB", "verify-ps1-73MB",
+         "verify-ps64-146MB", "verify-ps1-586MB"])
 def test_nontemporal_paths_match(L, B, ctx, ps, msl):
     """The paths chosen by the step's size: a decode step that may read more
     than 512 MB of rows (B x max_seq_len x 256 B) loads V and stores its
     partials non-temporally; at page size 64, from 256 MB, it loads V
     non-temporally with ordinary partial stores; a verify block from 4 MB
-    stores its partials non-temporally.  Declaring a larger max_seq_len for
+    stores its partials non-temporally, and above 512 MB also reads its rows
+    into the ring non-temporally.  Declaring a larger max_seq_len for
     small requests selects those paths at a size the oracle checks: each
     gives the bytes of the ordinary path (same arithmetic in the same order)
     over several partitions, and meets the oracle."""
